@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""GVA decode benchmark on one MI355X.
+
+A step is one pass of the decode hot path for one layer's compact cache:
+gva_append (one new token per sequence, RoPE on its positional key), then
+gva_rope_query (rotate the query's positional slice), then gva_decode
+(absorbed scores over V and k_r, online softmax, P.V, split-K merge).
+Consecutive steps visit R distinct cache replicas (layers) so every decode
+reads data that has not been touched for more than the 256 MB last-level
+cache; the default workload is B=16, S=4096, H=16, G=4, d_v=d_n=64, d_r=16,
+bf16 (the mid workload), on seeded synthetic data.
+
+Prints one JSON line. `value` = steps/s of the whole path (graph-replayed, so
+host launch overhead is excluded); the decode kernel's roofline is measured
+with HIP events around each gva_decode call on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "GVA decode steps/s + effective cache-read GB/s (% HBM peak), B=16 S=4096 bf16"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="mid_bf16")
+    p.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = enough for 512 MB)")
+    p.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--profile-decode", type=int, default=0,
+                   help="only run N eager decodes (for rocprofv3 runs) and exit")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "this decode path has no multi-GPU mode; see the sharding notes in the design doc.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import compact_kv_cache_amd as gva
+    import workloads as W
+    from compact_kv_cache_amd.cache import GvaCache
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS[args.workload]
+    assert not wl.ragged, "bench drives uniform-length workloads"
+    base = wl.rope_base
+    bpt = gva.gva_cache_bytes_per_token(wl.G, wl.d_v, wl.d_r, wl.dtype)
+    cache_bytes = wl.B * wl.S * bpt
+    R = args.replicas or max(2, math.ceil(512e6 / cache_bytes))
+    K, Wm = args.steps, args.warmup
+    total_steps = Wm + 3 * K + 8
+    per_rep = math.ceil(total_steps / R) + 1
+    cap = wl.S + per_rep
+
+    # ---- inputs (seeded, synthetic) -------------------------------------
+    inp = W.make_gva_inputs(wl)
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 77))
+    v_new = W.round_storage(rng.standard_normal((total_steps, wl.B, wl.G, 1, wl.d_v)), wl.dtype)
+    kr_new = W.round_storage(rng.standard_normal((total_steps, wl.B, 1, wl.d_r)), wl.dtype)
+    td = W.torch_dtype(wl.dtype)
+    to = lambda x: W.to_torch(x, wl.dtype).to(dev)  # noqa: E731
+    q_nope, q_rope, M = to(inp.q_nope), to(inp.q_rope), to(inp.M)
+    v_new_d, kr_new_d = to(v_new), to(kr_new)
+    q_rot = torch.empty_like(q_rope)
+    out = torch.empty(wl.B, wl.H, wl.d_v, dtype=td, device=dev)
+
+    caches = []
+    first = GvaCache(wl.B, wl.H, wl.G, wl.d_n, wl.d_v, wl.d_r, dtype=wl.dtype, capacity=cap,
+                     device=dev)
+    first.append(to(np.stack(inp.V)), to(np.stack(inp.kr)), base)
+    caches.append(first)
+    for _ in range(R - 1):
+        c = GvaCache(wl.B, wl.H, wl.G, wl.d_n, wl.d_v, wl.d_r, dtype=wl.dtype, capacity=cap,
+                     device=dev)
+        c.v_cache.copy_(first.v_cache)
+        c.kr_cache.copy_(first.kr_cache)
+        c.seq_lens.copy_(first.seq_lens)
+        caches.append(c)
+    del inp
+    n_host = [wl.S] * R
+    ws_bytes = max(gva.gva_decode_workspace_bytes(caches[0].shape(n, wl.split_tokens))
+                   for n in range(wl.S, cap + 1))
+    ws = torch.zeros(max(ws_bytes, 4) // 4 + 1, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def shape_at(r, n):
+        return caches[r].shape(n, wl.split_tokens)
+
+    def decode(r):
+        c = caches[r]
+        gva.gva_decode(shape_at(r, n_host[r]), q_nope, q_rot, M, c.v_cache, c.kr_cache,
+                       c.seq_lens, None, wl.scale, out, ws)
+
+    step_bytes = []
+
+    def step(i):
+        r = i % R
+        c = caches[r]
+        gva.gva_append(shape_at(r, c.capacity), v_new_d[i], kr_new_d[i], 1, c.seq_lens,
+                       c.v_cache, c.kr_cache, None, base)
+        n_host[r] += 1
+        gva.gva_rope_query(shape_at(r, n_host[r]), q_rope, q_rot, c.seq_lens, base)
+        decode(r)
+        step_bytes.append(wl.B * n_host[r] * bpt)
+
+    if args.profile_decode:
+        for i in range(args.profile_decode):
+            decode(i % R)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_decode": args.profile_decode, "replicas": R}))
+        return
+
+    i_step = 0
+    for _ in range(Wm):
+        step(i_step)
+        i_step += 1
+    torch.cuda.synchronize()
+
+    # ---- timed region 1: whole step (append + rope_query + decode) ---------
+    use_graph = not args.no_graph
+    step_bytes.clear()
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(K):
+                step(i_step)
+                i_step += 1
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_graph = e0.elapsed_time(e1) / K
+    else:
+        ms_graph = None
+    # eager timing of the same step sequence (host launch overhead included)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step(i_step)
+        i_step += 1
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t0) * 1e3 / K
+    ms_per_step = ms_graph if ms_graph is not None else ms_eager
+    mean_step_bytes = float(np.mean(step_bytes))
+
+    # ---- timed region 2: decode kernel alone, HIP events around each call --
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    dec_bytes = []
+    torch.cuda.synchronize()
+    for k in range(K):
+        r = k % R
+        evs[k][0].record(stream)
+        decode(r)
+        evs[k][1].record(stream)
+        dec_bytes.append(wl.B * n_host[r] * bpt)
+    torch.cuda.synchronize()
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_ms_mean = float(np.mean(dec_ms))
+    dec_bytes_mean = float(np.mean(dec_bytes))
+    achieved = dec_bytes_mean / (dec_ms_mean * 1e-3) / 1e9
+
+    # back-to-back decodes in one graph (kernel time + launch gaps)
+    ms_dec_graph = None
+    if use_graph:
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2):
+            for k in range(K):
+                decode(k % R)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g2.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_dec_graph = e0.elapsed_time(e1) / K
+
+    traffic = None  # filled from profiles only while the kernel source matches (see design doc)
+
+    result = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_per_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) caches and queries, M ~ N(0,1/64))",
+        "config": {"workload": f"{wl.name}: GVA decode step B={wl.B} S={wl.S} H={wl.H} "
+                               f"G={wl.G} d_n={wl.d_n} d_v={wl.d_v} d_r={wl.d_r} {wl.dtype}, "
+                               f"contiguous cache, {R} cold replicas",
+                   "B": wl.B, "S": wl.S, "H": wl.H, "G": wl.G, "d_v": wl.d_v, "d_r": wl.d_r,
+                   "replicas": R, "split_tokens": gva.gva_decode_split_tokens(shape_at(0, wl.S)),
+                   "graph": use_graph},
+        "cache_read_GBps": round(mean_step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "decode_us": round(dec_ms_mean * 1e3, 3),
+        "decode_graph_us": None if ms_dec_graph is None else round(ms_dec_graph * 1e3, 3),
+        "eager_ms_per_step": round(ms_eager, 6),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "bytes_per_launch": dec_bytes_mean},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, seconds: float):
+    """The CPU oracle as it stands, on a bounded sample of the same workload:
+    full decode steps (all B sequences, n = S + 1) repeated until `seconds`
+    of CPU time have passed."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    import workloads as W
+
+    inp = W.make_gva_inputs(wl, extra=1)
+    n = np.full(wl.B, wl.S + 1)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.gva_decode_step(inp.V, inp.kr, inp.q_nope, inp.q_rope, inp.M, n, wl.scale,
+                          wl.rope_base, wl.dtype)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(reps / el, 4), "unit": "steps/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reps} full oracle decode steps of {wl.name} (B={wl.B}, n={wl.S + 1}) "
+                      f"in {el:.1f} s, float64 numpy, {len(os.sched_getaffinity(0))} cpus visible"}
+
+
+if __name__ == "__main__":
+    main()

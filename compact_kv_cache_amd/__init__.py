@@ -1,0 +1,138 @@
+"""Grouped Value Attention (GVA) decode over a compact KV cache, for MI355X.
+
+Thin torch binding of the C ABI in include/gva.h: each function here checks
+and marshals its tensor arguments (device pointers, the current HIP stream)
+and calls the function of the same name in libgva.so. All arithmetic runs in
+the library's HIP kernels; torch only provides device memory and streams.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import GVA_BF16, GVA_F32, GvaShape
+
+__all__ = [
+    "GvaShape", "GVA_F32", "GVA_BF16", "GvaError", "make_shape", "lib",
+    "gva_append", "gva_rope_query", "gva_decode", "gva_gqa_ref_decode",
+    "gva_decode_workspace_bytes", "gva_decode_split_tokens", "gva_cache_bytes_per_token",
+    "gva_status_string", "gva_abi_version", "workspace_for",
+]
+
+lib = _lib.load()
+
+_DTYPES = {"bf16": GVA_BF16, "f32": GVA_F32, torch.bfloat16: GVA_BF16, torch.float32: GVA_F32}
+_TORCH = {GVA_BF16: torch.bfloat16, GVA_F32: torch.float32}
+
+
+class GvaError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        name = lib.gva_status_string(status).decode()
+        detail = lib.gva_last_error().decode()
+        super().__init__(f"{fn}: {name}: {detail}")
+
+
+def make_shape(B: int, H: int, G: int, d_n: int, d_v: int, d_r: int, *, capacity: int = 0,
+               max_seq_len: int = 0, block_size: int = 0, num_blocks: int = 0,
+               max_blocks_per_seq: int = 0, split_tokens: int = 0, dtype="bf16") -> GvaShape:
+    return GvaShape(B, H, G, d_n, d_v, d_r, capacity, max_seq_len, block_size, num_blocks,
+                    max_blocks_per_seq, split_tokens, _DTYPES[dtype])
+
+
+def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype], what: str):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, fn: str):
+    if status != _lib.GVA_OK:
+        raise GvaError(status, fn)
+
+
+def gva_append(shape: GvaShape, v_new, kr_new, n_new: int, seq_lens, v_cache, kr_cache,
+               block_table=None, rope_base: float = 10000.0, stream=None) -> None:
+    dt = _TORCH.get(shape.dtype)
+    _check(lib.gva_append(shape, _ptr(v_new, dt, "v_new"), _ptr(kr_new, dt, "kr_new"), int(n_new),
+                          _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(v_cache, dt, "v_cache"),
+                          _ptr(kr_cache, dt, "kr_cache"),
+                          _ptr(block_table, torch.int32, "block_table"), float(rope_base),
+                          _stream(stream)), "gva_append")
+
+
+def gva_rope_query(shape: GvaShape, q_rope_in, q_rope_out, seq_lens, rope_base: float = 10000.0,
+                   stream=None) -> None:
+    dt = _TORCH.get(shape.dtype)
+    _check(lib.gva_rope_query(shape, _ptr(q_rope_in, dt, "q_rope_in"),
+                              _ptr(q_rope_out, dt, "q_rope_out"),
+                              _ptr(seq_lens, torch.int32, "seq_lens"), float(rope_base),
+                              _stream(stream)), "gva_rope_query")
+
+
+def gva_decode(shape: GvaShape, q_nope, q_rope, M, v_cache, kr_cache, seq_lens, block_table,
+               scale: float, out, workspace=None, stream=None) -> None:
+    dt = _TORCH.get(shape.dtype)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gva_decode(shape, _ptr(q_nope, dt, "q_nope"), _ptr(q_rope, dt, "q_rope"),
+                          _ptr(M, dt, "M"), _ptr(v_cache, dt, "v_cache"),
+                          _ptr(kr_cache, dt, "kr_cache"), _ptr(seq_lens, torch.int32, "seq_lens"),
+                          _ptr(block_table, torch.int32, "block_table"), float(scale),
+                          _ptr(out, dt, "out"), _ptr(workspace, None, "workspace"), ws_bytes,
+                          _stream(stream)), "gva_decode")
+
+
+def gva_gqa_ref_decode(shape: GvaShape, q, k_cache, v_cache, seq_lens, block_table, scale: float,
+                       out, workspace=None, stream=None) -> None:
+    dt = _TORCH.get(shape.dtype)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gva_gqa_ref_decode(shape, _ptr(q, dt, "q"), _ptr(k_cache, dt, "k_cache"),
+                                  _ptr(v_cache, dt, "v_cache"),
+                                  _ptr(seq_lens, torch.int32, "seq_lens"),
+                                  _ptr(block_table, torch.int32, "block_table"), float(scale),
+                                  _ptr(out, dt, "out"), _ptr(workspace, None, "workspace"),
+                                  ws_bytes, _stream(stream)), "gva_gqa_ref_decode")
+
+
+def gva_decode_workspace_bytes(shape: GvaShape) -> int:
+    return int(lib.gva_decode_workspace_bytes(shape))
+
+
+def gva_decode_split_tokens(shape: GvaShape) -> int:
+    return int(lib.gva_decode_split_tokens(shape))
+
+
+def gva_cache_bytes_per_token(G: int, d_v: int, d_r: int, dtype="bf16") -> int:
+    return int(lib.gva_cache_bytes_per_token(G, d_v, d_r, _DTYPES[dtype]))
+
+
+def gva_status_string(status: int) -> str:
+    return lib.gva_status_string(status).decode()
+
+
+def gva_abi_version() -> int:
+    return int(lib.gva_abi_version())
+
+
+def workspace_for(shape: GvaShape, device="cuda") -> Optional[torch.Tensor]:
+    """Zero-filled device workspace of the size gva_decode needs (None if none)."""
+    n = gva_decode_workspace_bytes(shape)
+    if n == 0:
+        return None
+    return torch.zeros((n + 3) // 4, dtype=torch.float32, device=device)

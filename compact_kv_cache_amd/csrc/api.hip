@@ -1,0 +1,259 @@
+// C ABI of the GVA decode library: argument validation, split-K planning and
+// dispatch to the kernels. Nothing here allocates device memory.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/gva.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gva_status fail(gva_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+gva_status ok() {
+  g_last_error.clear();
+  return GVA_OK;
+}
+
+gva_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(GVA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shape checks common to every call. `gqa` selects the GQA comparison rules.
+gva_status check_shape(const gva_shape* s, bool gqa) {
+  if (!s) return fail(GVA_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (s->B < 1 || s->H < 1 || s->G < 1)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "B, H, G must be >= 1 (got %d, %d, %d)", s->B, s->H, s->G);
+  if (s->H % s->G != 0)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "H (%d) must be a multiple of G (%d)", s->H, s->G);
+  const int hpg = s->H / s->G;
+  if (hpg != 1 && hpg != 2 && hpg != 4)
+    return fail(GVA_ERR_UNSUPPORTED, "H/G = %d; built for 1, 2 or 4 heads per group", hpg);
+  if (s->d_n != 64 || s->d_v != 64)
+    return fail(GVA_ERR_UNSUPPORTED, "d_n = %d, d_v = %d; built for d_n = d_v = 64", s->d_n, s->d_v);
+  if (s->d_r < 0 || s->d_r % 2 != 0)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "d_r = %d must be even and >= 0", s->d_r);
+  if (s->d_r % 8 != 0 || s->d_r > 32)
+    return fail(GVA_ERR_UNSUPPORTED, "d_r = %d; built for 0, 8, 16, 24, 32", s->d_r);
+  if (gqa && s->d_r != 0)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "GQA reference needs d_r == 0 (got %d)", s->d_r);
+  if (s->dtype != GVA_F32 && s->dtype != GVA_BF16)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "dtype %d is not a gva_dtype", s->dtype);
+  if (s->max_seq_len < 0) return fail(GVA_ERR_INVALID_ARGUMENT, "max_seq_len < 0");
+  if (s->split_tokens < 0 || s->split_tokens % 64 != 0)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "split_tokens = %d must be 0 or a positive multiple of 64",
+                s->split_tokens);
+  if (s->block_size == 0) {
+    if (s->capacity < 1) return fail(GVA_ERR_INVALID_ARGUMENT, "contiguous cache needs capacity >= 1");
+    if (s->max_seq_len > s->capacity)
+      return fail(GVA_ERR_INVALID_ARGUMENT, "max_seq_len %d exceeds capacity %d", s->max_seq_len,
+                  s->capacity);
+  } else if (s->block_size == 64) {
+    if (s->num_blocks < 1 || s->max_blocks_per_seq < 1)
+      return fail(GVA_ERR_INVALID_ARGUMENT, "paged cache needs num_blocks >= 1 and max_blocks_per_seq >= 1");
+    if ((int64_t)s->max_seq_len > (int64_t)s->max_blocks_per_seq * 64)
+      return fail(GVA_ERR_INVALID_ARGUMENT, "max_seq_len %d exceeds max_blocks_per_seq * 64", s->max_seq_len);
+    if ((int64_t)s->max_blocks_per_seq * 64 > INT32_MAX)
+      return fail(GVA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq too large");
+  } else {
+    return fail(GVA_ERR_UNSUPPORTED, "block_size %d; built for 0 (contiguous) or 64", s->block_size);
+  }
+  return GVA_OK;
+}
+
+int resolve_split(const gva_shape* s) {
+  if (s->split_tokens > 0) return s->split_tokens;
+  // Aim for about 1024 workgroups of (sequence, group, partition) so every
+  // compute unit holds several, without partitions shorter than 256 tokens.
+  const int64_t pairs = (int64_t)s->B * s->G;
+  const int64_t want_parts = (1024 + pairs - 1) / pairs;
+  int64_t split = (s->max_seq_len + want_parts - 1) / want_parts;
+  split = ((split + 63) / 64) * 64;
+  if (split < 256) split = 256;
+  return (int)split;
+}
+
+int n_splits(const gva_shape* s, int split) {
+  return s->max_seq_len <= 0 ? 1 : (s->max_seq_len + split - 1) / split;
+}
+
+size_t workspace_for(const gva_shape* s) {
+  const int split = resolve_split(s);
+  return gva::ws_total_bytes(s->B, s->H, s->G, n_splits(s, split));
+}
+
+void set_workspace(gva::DecodeLaunch& a, void* workspace) {
+  if (a.n_split <= 1 || !workspace) return;
+  char* base = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<int32_t*>(base);
+  a.ws_o = reinterpret_cast<float*>(base + gva::ws_counter_bytes(a.B, a.G));
+  a.ws_ml = a.ws_o + (size_t)a.B * a.H * a.n_split * 64;
+}
+
+gva::DecodeLaunch make_decode(const gva_shape* s) {
+  gva::DecodeLaunch a{};
+  a.B = s->B;
+  a.H = s->H;
+  a.G = s->G;
+  a.d_r = s->d_r;
+  a.capacity = s->capacity;
+  a.max_seq_len = s->max_seq_len;
+  a.num_blocks = s->num_blocks;
+  a.max_blocks = s->max_blocks_per_seq;
+  a.split = resolve_split(s);
+  a.n_split = n_splits(s, a.split);
+  a.paged = s->block_size != 0;
+  a.bf16 = s->dtype == GVA_BF16;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+gva_status gva_append(const gva_shape* shape, const void* v_new, const void* kr_new, int32_t n_new,
+                      int32_t* seq_lens, void* v_cache, void* kr_cache, const int32_t* block_table,
+                      float rope_base, hipStream_t stream) {
+  gva_status st = check_shape(shape, false);
+  if (st != GVA_OK) return st;
+  if (n_new < 1) return fail(GVA_ERR_INVALID_ARGUMENT, "n_new must be >= 1 (got %d)", n_new);
+  if (!v_new || !seq_lens || !v_cache)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "v_new, seq_lens and v_cache must be non-NULL");
+  if (shape->d_r > 0 && (!kr_new || !kr_cache))
+    return fail(GVA_ERR_INVALID_ARGUMENT, "kr_new and kr_cache must be non-NULL when d_r > 0");
+  if (shape->block_size != 0 && !block_table)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "paged cache needs a block_table");
+  if (!(rope_base > 0.f)) return fail(GVA_ERR_INVALID_ARGUMENT, "rope_base must be > 0");
+  gva::AppendLaunch a{};
+  a.B = shape->B;
+  a.G = shape->G;
+  a.d_r = shape->d_r;
+  a.n_new = n_new;
+  a.capacity = shape->capacity;
+  a.num_blocks = shape->num_blocks;
+  a.max_blocks = shape->max_blocks_per_seq;
+  a.paged = shape->block_size != 0;
+  a.bf16 = shape->dtype == GVA_BF16;
+  a.v_new = v_new;
+  a.kr_new = kr_new;
+  a.seq_lens = seq_lens;
+  a.v_cache = v_cache;
+  a.kr_cache = kr_cache;
+  a.block_table = block_table;
+  a.rope_base = rope_base;
+  return hip_status(gva::launch_append(a, stream), "gva_append launch");
+}
+
+gva_status gva_rope_query(const gva_shape* shape, const void* q_rope_in, void* q_rope_out,
+                          const int32_t* seq_lens, float rope_base, hipStream_t stream) {
+  gva_status st = check_shape(shape, false);
+  if (st != GVA_OK) return st;
+  if (shape->d_r == 0) return ok();
+  if (!q_rope_in || !q_rope_out || !seq_lens)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "q_rope_in, q_rope_out and seq_lens must be non-NULL");
+  if (!(rope_base > 0.f)) return fail(GVA_ERR_INVALID_ARGUMENT, "rope_base must be > 0");
+  gva::RopeQueryLaunch a{};
+  a.B = shape->B;
+  a.H = shape->H;
+  a.d_r = shape->d_r;
+  a.bf16 = shape->dtype == GVA_BF16;
+  a.q_in = q_rope_in;
+  a.q_out = q_rope_out;
+  a.seq_lens = seq_lens;
+  a.rope_base = rope_base;
+  return hip_status(gva::launch_rope_query(a, stream), "gva_rope_query launch");
+}
+
+gva_status gva_decode(const gva_shape* shape, const void* q_nope, const void* q_rope, const void* M,
+                      const void* v_cache, const void* kr_cache, const int32_t* seq_lens,
+                      const int32_t* block_table, float scale, void* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  gva_status st = check_shape(shape, false);
+  if (st != GVA_OK) return st;
+  if (!q_nope || !M || !v_cache || !seq_lens || !out)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "q_nope, M, v_cache, seq_lens and out must be non-NULL");
+  if (shape->d_r > 0 && (!q_rope || !kr_cache))
+    return fail(GVA_ERR_INVALID_ARGUMENT, "q_rope and kr_cache must be non-NULL when d_r > 0");
+  if (shape->block_size != 0 && !block_table)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "paged cache needs a block_table");
+  const size_t need = workspace_for(shape);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  gva::DecodeLaunch a = make_decode(shape);
+  a.q_nope = q_nope;
+  a.q_rope = q_rope;
+  a.M = M;
+  a.v_cache = v_cache;
+  a.kr_cache = kr_cache;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.scale = scale;
+  a.out = out;
+  set_workspace(a, workspace);
+  return hip_status(gva::launch_decode_valu(a, stream), "gva_decode launch");
+}
+
+gva_status gva_gqa_ref_decode(const gva_shape* shape, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                              float scale, void* out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  gva_status st = check_shape(shape, true);
+  if (st != GVA_OK) return st;
+  if (!q || !k_cache || !v_cache || !seq_lens || !out)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache, seq_lens and out must be non-NULL");
+  if (shape->block_size != 0 && !block_table)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "paged cache needs a block_table");
+  const size_t need = workspace_for(shape);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  (void)scale;
+  (void)stream;
+  return fail(GVA_ERR_UNSUPPORTED, "GQA reference kernel not built yet");
+}
+
+size_t gva_decode_workspace_bytes(const gva_shape* shape) {
+  if (check_shape(shape, false) != GVA_OK && check_shape(shape, true) != GVA_OK) return 0;
+  return workspace_for(shape);
+}
+
+int32_t gva_decode_split_tokens(const gva_shape* shape) {
+  if (check_shape(shape, false) != GVA_OK && check_shape(shape, true) != GVA_OK) return 0;
+  return resolve_split(shape);
+}
+
+size_t gva_cache_bytes_per_token(int32_t G, int32_t d_v, int32_t d_r, int32_t dtype) {
+  size_t el = dtype == GVA_F32 ? 4 : dtype == GVA_BF16 ? 2 : 0;
+  if (G < 0 || d_v < 0 || d_r < 0) return 0;
+  return ((size_t)G * d_v + d_r) * el;
+}
+
+const char* gva_status_string(gva_status status) {
+  switch (status) {
+    case GVA_OK: return "GVA_OK";
+    case GVA_ERR_INVALID_ARGUMENT: return "GVA_ERR_INVALID_ARGUMENT";
+    case GVA_ERR_UNSUPPORTED: return "GVA_ERR_UNSUPPORTED";
+    case GVA_ERR_WORKSPACE: return "GVA_ERR_WORKSPACE";
+    case GVA_ERR_HIP: return "GVA_ERR_HIP";
+  }
+  return "GVA_ERR_UNKNOWN";
+}
+
+const char* gva_last_error(void) { return g_last_error.c_str(); }
+
+int32_t gva_abi_version(void) { return 1; }
+
+}  // extern "C"

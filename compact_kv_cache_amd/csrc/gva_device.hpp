@@ -1,0 +1,146 @@
+// Device-side helpers shared by the GVA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gva {
+
+constexpr int kD = 64;          // d_n = d_v built here
+constexpr int kTile = 64;       // tokens per tile == paged block size
+constexpr int kBlock = 64;      // paged block size (tokens)
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// Scalar loads / stores in the call dtype (float or __bf16), as float.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// Correctly rounded (to nearest, ties to even) conversion of a double.
+// For bf16: round to odd into binary32 first (truncate, then set the last bit
+// when inexact), which has 16 more fraction bits than bf16, then round to
+// nearest even; the composition equals a single correct rounding.
+template <typename T> __device__ __forceinline__ T from_f64(double x);
+template <> __device__ __forceinline__ float from_f64<float>(double x) { return (float)x; }
+template <> __device__ __forceinline__ __bf16 from_f64<__bf16>(double x) {
+  float f = __double2float_rz(x);
+  if ((double)f != x && !__builtin_isnan(x)) f = __uint_as_float(__float_as_uint(f) | 1u);
+  return (__bf16)f;
+}
+
+// ---------------------------------------------------------------------------
+// RoPE on one channel pair (2i, 2i+1) at position pos: counter-clockwise turn
+// by pos * base^(-2i/d_r), in double precision.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rope_pair(double x0, double x1, double pos, int i, int d_r,
+                                          double base, double& y0, double& y1) {
+  const double theta = pow(base, -2.0 * (double)i / (double)d_r);
+  double s, c;
+  sincos(pos * theta, &s, &c);
+  y0 = x0 * c - x1 * s;
+  y1 = x0 * s + x1 * c;
+}
+
+// ---------------------------------------------------------------------------
+// Wave-wide reductions (64 lanes).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Cache addressing. Offsets are element offsets (64-bit).
+// ---------------------------------------------------------------------------
+struct CacheGeom {
+  int G, d_r, capacity, num_blocks, max_blocks;
+  const int32_t* block_table;  // null = contiguous
+};
+
+// Pool block of token t of sequence b, or -1 if the table entry is invalid.
+__device__ __forceinline__ int page_of(const CacheGeom& c, int b, int t) {
+  const int j = t / kBlock;
+  if (j >= c.max_blocks) return -1;
+  const int blk = c.block_table[(size_t)b * c.max_blocks + j];
+  return (blk >= 0 && blk < c.num_blocks) ? blk : -1;
+}
+
+// Offset of row (b, g, t) in a [.., G, .., d] value-like cache (d = kD); -1 if
+// the row is outside the cache.
+template <bool PAGED>
+__device__ __forceinline__ int64_t v_row(const CacheGeom& c, int b, int g, int t) {
+  if (PAGED) {
+    const int blk = page_of(c, b, t);
+    if (blk < 0) return -1;
+    return (((int64_t)blk * c.G + g) * kBlock + (t % kBlock)) * kD;
+  } else {
+    if (t >= c.capacity) return -1;
+    return (((int64_t)b * c.G + g) * c.capacity + t) * kD;
+  }
+}
+
+template <bool PAGED>
+__device__ __forceinline__ int64_t kr_row(const CacheGeom& c, int b, int t) {
+  if (PAGED) {
+    const int blk = page_of(c, b, t);
+    if (blk < 0) return -1;
+    return ((int64_t)blk * kBlock + (t % kBlock)) * c.d_r;
+  } else {
+    if (t >= c.capacity) return -1;
+    return ((int64_t)b * c.capacity + t) * c.d_r;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K arrival: every workgroup of one (sequence, group) publishes its
+// partial result, then bumps an arrival counter; the one that arrives last
+// merges all partials and resets the counter to zero for the next call.
+// Must be reached by every thread of the workgroup. Returns the same value in
+// all threads.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool arrive_last(int32_t* counter, int n_parts) {
+  __shared__ int s_last;
+  __threadfence();  // release: this workgroup's partials are visible device-wide
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old == n_parts - 1);
+  }
+  __syncthreads();
+  const bool last = s_last != 0;
+  if (last) __threadfence();  // acquire: every other partial is visible here
+  return last;
+}
+
+__device__ __forceinline__ void reset_counter(int32_t* counter) {
+  __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Log-sum-exp merge of n_parts partials of one head for channel d:
+// out = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s, M = max_s m_s, with
+// m_s in log2 units and o_s unnormalized.
+__device__ __forceinline__ float merge_partials(const float* o, const float* ml, int64_t slot0,
+                                                int n_parts, int d) {
+  float M = -INFINITY;
+  for (int s = 0; s < n_parts; ++s) M = fmaxf(M, ml[2 * (slot0 + s)]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < n_parts; ++s) {
+    const float w = exp2f(ml[2 * (slot0 + s)] - M);
+    num = fmaf(w, o[(slot0 + s) * kD + d], num);
+    den = fmaf(w, ml[2 * (slot0 + s) + 1], den);
+  }
+  return den > 0.f ? num / den : 0.f;
+}
+
+}  // namespace gva

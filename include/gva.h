@@ -1,0 +1,216 @@
+/*
+ * gva.h - C ABI of the Grouped Value Attention (GVA) decode library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * GVA keeps a compact KV cache: per layer and sequence only the grouped
+ * values V_g [G, S, d_v] and ONE positional key k_r [S, d_r] shared by all
+ * query heads. Query head h rebuilds its content key as K_h = V_g(h) M_h and,
+ * at decode, folds M_h into its query instead (q'_h = M_h q_nope,h), so the
+ * kernels score q'_h . V_g(h)[t] + q_rope,h . k_r[t] without building keys.
+ *
+ * Pages cited (title, where it lives):
+ *   [digest]   "Grouped Value Attention:通过按需 key 重建实现高效 KV 缓存",
+ *              ai-feeds.com paper digest of arXiv 2609.13285
+ *   [explain]  popular explainer of the same paper, m.szthrk.cn
+ *   [abstract] "Grouped Value Attention: Efficient KV Caching via On-Demand
+ *              Key Reconstruction", Hugging Face papers page
+ *   [review]   "[논문리뷰] Grouped Value Attention: ...", blog.secrett2633.cloud
+ *   [gqa]      "GQA 分组查询注意力：KV Cache 与模型质量的折中", charlestar.github.io
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors), row-major, densely packed, in the call dtype unless stated.
+ *     `shape` itself is a host pointer read during the call only.
+ *   - The caller owns every buffer. The library allocates no memory and keeps
+ *     no pointer after returning.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream); no
+ *     call synchronizes the device.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     rejected call returns a status other than GVA_OK and enqueues nothing.
+ *     gva_last_error() then describes the problem (thread-local text).
+ *   - Device data that the host cannot see (seq_lens, block_table) is
+ *     clamped in the kernels so that a contract violation never touches
+ *     memory outside the buffers described by `shape`; the results of such
+ *     a call are unspecified.
+ *   - Head h reads value group h / (H/G) (contiguous head blocks, as in the
+ *     [gqa] tutorial's structure diagram).
+ *   - RoPE turns channel pairs (2i, 2i+1) by pos * theta_i with
+ *     theta_i = rope_base^(-2i/d_r); angles and the rotation are computed in
+ *     double precision and rounded once (to nearest even) to the cache dtype.
+ *     The pages fix no pairing; they require the cached key and the query to
+ *     share one convention ([gqa] section on RoPE and the KV cache).
+ */
+#ifndef GVA_H
+#define GVA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gva_status {
+  GVA_OK = 0,
+  GVA_ERR_INVALID_ARGUMENT = 1, /* null pointer, inconsistent sizes          */
+  GVA_ERR_UNSUPPORTED = 2,      /* valid but not built (e.g. d_v != 64)      */
+  GVA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than needed  */
+  GVA_ERR_HIP = 4               /* a HIP runtime call or launch failed       */
+} gva_status;
+
+typedef enum gva_dtype {
+  GVA_F32 = 0,  /* IEEE binary32 everywhere                                   */
+  GVA_BF16 = 1  /* bfloat16 storage; every accumulation is fp32               */
+} gva_dtype;
+
+/*
+ * Problem description shared by all calls.
+ *   B, H, G          sequences, query heads, value groups (H % G == 0,
+ *                    H/G in {1, 2, 4})
+ *   d_n, d_v         content-query and value widths (this build: 64, 64)
+ *   d_r              shared positional-key width (0, 8, 16, 24 or 32)
+ *   capacity         contiguous cache: token slots per sequence;
+ *                    paged cache: ignored
+ *   max_seq_len      host-side upper bound of seq_lens[b] during the call
+ *                    (sizes the decode grid); tokens beyond it are ignored.
+ *                    Must be <= capacity (contiguous) or
+ *                    <= max_blocks_per_seq * block_size (paged).
+ *   block_size       0 = contiguous cache; 64 = paged cache of 64-token blocks
+ *   num_blocks       paged: blocks in the pool
+ *   max_blocks_per_seq  paged: row stride of block_table
+ *   split_tokens     split-K partition length in tokens for decode
+ *                    (0 = automatic; otherwise a positive multiple of 64)
+ *   dtype            storage dtype of q, M, caches and out
+ *
+ * Cache layouts (call dtype):
+ *   contiguous  v_cache  [B][G][capacity][d_v]    kr_cache [B][capacity][d_r]
+ *   paged       v_cache  [num_blocks][G][64][d_v] kr_cache [num_blocks][64][d_r]
+ *               block_table int32 [B][max_blocks_per_seq]: entry j of row b is
+ *               the pool block holding tokens [64j, 64j+64) of sequence b.
+ */
+typedef struct gva_shape {
+  int32_t B, H, G;
+  int32_t d_n, d_v, d_r;
+  int32_t capacity;
+  int32_t max_seq_len;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t split_tokens;
+  int32_t dtype; /* a gva_dtype value */
+} gva_shape;
+
+/*
+ * gva_append - write new tokens into the compact cache.
+ * Follows the decode loop of [gqa] (section on why the KV cache keeps
+ * growing, and the cache-lifecycle list of the RoPE section): each new token
+ * stores its state once and advances the sequence position. What is stored
+ * is GVA's persistent cache: the grouped values (never rotated) and the one
+ * positional key after RoPE ([digest] 方法 / GVA 核心流程; [explain] 位置信息
+ * 怎么办; [review] Decoupled RoPE).
+ *   v_new     [B][G][n_new][d_v]   values of the new tokens
+ *   kr_new    [B][n_new][d_r]      positional keys BEFORE RoPE (may be NULL
+ *                                  when d_r == 0)
+ *   n_new     tokens appended to every sequence (>= 1)
+ *   seq_lens  int32 [B], in/out: token t of the new block lands at position
+ *             seq_lens[b] + t and is rotated by that position; on completion
+ *             seq_lens[b] += n_new.
+ *   block_table  NULL for a contiguous cache (shape->block_size == 0).
+ * Writes past the cache capacity (or into a block id outside the pool) are
+ * skipped; seq_lens is then clamped to the capacity.
+ */
+gva_status gva_append(const gva_shape* shape, const void* v_new, const void* kr_new,
+                      int32_t n_new, int32_t* seq_lens, void* v_cache, void* kr_cache,
+                      const int32_t* block_table, float rope_base, hipStream_t stream);
+
+/*
+ * gva_rope_query - rotate the positional slice of the decode queries.
+ * The query of the newest token sits at position seq_lens[b] - 1 (it reads the
+ * earlier tokens and itself, [gqa] section on cache growth); only the d_r
+ * positional channels are rotated ([review] Decoupled RoPE).
+ *   q_rope_in, q_rope_out  [B][H][d_r]  (may alias)
+ * A sequence with seq_lens[b] <= 0 is rotated by position 0.
+ */
+gva_status gva_rope_query(const gva_shape* shape, const void* q_rope_in, void* q_rope_out,
+                          const int32_t* seq_lens, float rope_base, hipStream_t stream);
+
+/*
+ * gva_decode - one decode step of GVA attention over the compact cache.
+ * Computes, for every sequence b and head h with n = seq_lens[b] tokens,
+ *   s_t   = scale * ( (M_h q_nope[b,h]) . V[b, g(h), t] + q_rope[b,h] . k_r[b, t] )
+ *   out[b,h] = sum_t softmax(s)_t V[b, g(h), t]
+ * which equals softmax attention with the materialized keys
+ * K_h = [V_g(h) M_h || k_r] ([digest] 方法: Q' = Q M^T absorption and the
+ * value-weighted output; [explain] 正式方案; [review] 3. Method & Key
+ * Results; [abstract]). Content keys are never formed: M_h is folded into
+ * the query in the kernel prologue.
+ *   q_nope   [B][H][d_n]      content slice of the queries
+ *   q_rope   [B][H][d_r]      positional slice, ALREADY rotated (see
+ *                             gva_rope_query); NULL allowed when d_r == 0
+ *   M        [H][d_v][d_n]    reconstruction maps (K_h = V_g(h) M_h)
+ *   v_cache, kr_cache, block_table   as described at gva_shape
+ *   seq_lens int32 [B]        tokens to attend (the query's own included)
+ *   scale    softmax scale (e.g. 1/sqrt(d_n + d_r))
+ *   out      [B][H][d_v]      call dtype; rows with seq_lens[b] <= 0 are zero
+ *   workspace, workspace_bytes   device scratch of at least
+ *            gva_decode_workspace_bytes(shape) bytes (may be NULL/0 when that
+ *            is 0). It must be zero-filled before its first use; every call
+ *            that completes leaves it ready for the next one (its arrival
+ *            counters return to zero). Calls that overlap in time need
+ *            distinct workspaces.
+ * Long sequences are split into partitions of split_tokens tokens; each
+ * partition's workgroups write a partial result (unnormalized output, running
+ * max, running sum) and the last one to finish merges them with a
+ * log-sum-exp combine inside the same kernel launch.
+ */
+gva_status gva_decode(const gva_shape* shape, const void* q_nope, const void* q_rope,
+                      const void* M, const void* v_cache, const void* kr_cache,
+                      const int32_t* seq_lens, const int32_t* block_table, float scale,
+                      void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gva_gqa_ref_decode - plain grouped-query attention decode over a K+V cache
+ * of the same layout, the comparison point for bytes and time. GQA stores a
+ * key and a value row per group and token ([gqa] sections on the K/V cache
+ * shapes and one GQA computation; heads read their group's K/V through the
+ * head map without copying the cache, as that page asks of fast kernels).
+ *   shape    d_r must be 0 and d_n == d_v (= d_h)
+ *   q        [B][H][d_h]      queries, already rotated
+ *   k_cache, v_cache          [B][G][capacity][d_h] or paged
+ *                             [num_blocks][G][64][d_h]; K already rotated
+ *   other arguments as for gva_decode (same workspace size rule).
+ */
+gva_status gva_gqa_ref_decode(const gva_shape* shape, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* seq_lens,
+                              const int32_t* block_table, float scale, void* out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace gva_decode / gva_gqa_ref_decode need for
+ * `shape` (0 when no sequence is split). Returns 0 for an invalid shape. */
+size_t gva_decode_workspace_bytes(const gva_shape* shape);
+
+/* Split-K partition length (tokens) that gva_decode will use for `shape`
+ * (resolves split_tokens == 0). Returns 0 for an invalid shape. */
+int32_t gva_decode_split_tokens(const gva_shape* shape);
+
+/* Persistent cache bytes per token per layer: (G * d_v + d_r) * sizeof(dtype),
+ * G value rows plus the one shared positional key ([explain] section on the
+ * savings; [review] Decoupled RoPE). Returns 0 for an invalid dtype. */
+size_t gva_cache_bytes_per_token(int32_t G, int32_t d_v, int32_t d_r, int32_t dtype);
+
+/* Static description of a status code. */
+const char* gva_status_string(gva_status status);
+
+/* Thread-local description of the most recent failed call on this thread
+ * ("" if none). Valid until the next call on the same thread. */
+const char* gva_last_error(void);
+
+/* Library ABI version (incremented on incompatible changes). */
+int32_t gva_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GVA_H */
