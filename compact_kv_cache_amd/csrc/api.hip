@@ -2,6 +2,7 @@
 // dispatch to the kernels. Nothing here allocates device memory.
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "../../include/gva.h"
@@ -75,14 +76,14 @@ gva_status check_shape(const gva_shape* s, bool gqa) {
 
 int resolve_split(const gva_shape* s) {
   if (s->split_tokens > 0) return s->split_tokens;
-  // Aim for about 1024 workgroups of (sequence, group, partition) so every
-  // compute unit holds several, without partitions shorter than 256 tokens.
-  const int64_t pairs = (int64_t)s->B * s->G;
-  const int64_t want_parts = (1024 + pairs - 1) / pairs;
-  int64_t split = (s->max_seq_len + want_parts - 1) / want_parts;
-  split = ((split + 63) / 64) * 64;
-  if (split < 256) split = 256;
-  return (int)split;
+  // Aim for about 512 workgroups of (sequence, partition, four groups), i.e.
+  // two per compute unit, each streaming whole 64-token tiles.
+  const int64_t base = (int64_t)s->B * ((s->G + 3) / 4);
+  const int64_t want_parts = (512 + base - 1) / base;
+  const int64_t tiles = (s->max_seq_len + 63) / 64;
+  int64_t tiles_per = (tiles + want_parts - 1) / want_parts;
+  if (tiles_per < 1) tiles_per = 1;
+  return (int)(tiles_per * 64);
 }
 
 int n_splits(const gva_shape* s, int split) {
@@ -100,6 +101,16 @@ void set_workspace(gva::DecodeLaunch& a, void* workspace) {
   a.counters = reinterpret_cast<int32_t*>(base);
   a.ws_o = reinterpret_cast<float*>(base + gva::ws_counter_bytes(a.B, a.G));
   a.ws_ml = a.ws_o + (size_t)a.B * a.H * a.n_split * 64;
+}
+
+// GVA_FORCE_VALU=1 routes bf16 decodes to the vector-ALU kernel (used to
+// cross-check the two kernels against each other).
+bool force_valu() {
+  static const bool v = [] {
+    const char* e = getenv("GVA_FORCE_VALU");
+    return e && e[0] == '1';
+  }();
+  return v;
 }
 
 gva::DecodeLaunch make_decode(const gva_shape* s) {
@@ -203,7 +214,9 @@ gva_status gva_decode(const gva_shape* shape, const void* q_nope, const void* q_
   a.scale = scale;
   a.out = out;
   set_workspace(a, workspace);
-  return hip_status(gva::launch_decode_valu(a, stream), "gva_decode launch");
+  const hipError_t e = (a.bf16 && !force_valu()) ? gva::launch_decode_mfma(a, stream)
+                                                 : gva::launch_decode_valu(a, stream);
+  return hip_status(e, "gva_decode launch");
 }
 
 gva_status gva_gqa_ref_decode(const gva_shape* shape, const void* q, const void* k_cache,
@@ -216,13 +229,22 @@ gva_status gva_gqa_ref_decode(const gva_shape* shape, const void* q, const void*
     return fail(GVA_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache, seq_lens and out must be non-NULL");
   if (shape->block_size != 0 && !block_table)
     return fail(GVA_ERR_INVALID_ARGUMENT, "paged cache needs a block_table");
+  if (shape->dtype != GVA_BF16)
+    return fail(GVA_ERR_UNSUPPORTED, "GQA reference is built for bf16 caches only");
   const size_t need = workspace_for(shape);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
-  (void)scale;
-  (void)stream;
-  return fail(GVA_ERR_UNSUPPORTED, "GQA reference kernel not built yet");
+  gva::DecodeLaunch a = make_decode(shape);
+  a.q_nope = q;
+  a.v_cache = v_cache;
+  a.kr_cache = k_cache;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.scale = scale;
+  a.out = out;
+  set_workspace(a, workspace);
+  return hip_status(gva::launch_gqa_mfma(a, stream), "gva_gqa_ref_decode launch");
 }
 
 size_t gva_decode_workspace_bytes(const gva_shape* shape) {

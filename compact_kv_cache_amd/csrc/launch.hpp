@@ -60,5 +60,7 @@ inline size_t ws_total_bytes(int B, int H, int G, int n_split) {
 hipError_t launch_append(const AppendLaunch& a, hipStream_t s);
 hipError_t launch_rope_query(const RopeQueryLaunch& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeLaunch& a, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeLaunch& a, hipStream_t s);  // bf16 only
+hipError_t launch_gqa_mfma(const DecodeLaunch& a, hipStream_t s);     // bf16 only
 
 }  // namespace gva

@@ -260,3 +260,51 @@ def test_decode_mid_bf16_end_to_end_steps():
         ref = O.gva_decode_step(inp.V, inp.kr, inp.q_nope, inp.q_rope, inp.M,
                                 np.full(wl.B, n), wl.scale, BASE, "bf16")
         S.assert_close(S.host(out), ref, "bf16", f"mid e2e step {i}")
+
+
+# ---------------------------------------------------------------------------
+# GQA comparison kernel
+# ---------------------------------------------------------------------------
+
+def _gqa_run(wl, lens, *, paged=False, split=0, seed=0):
+    q, K, V = W.make_gqa_inputs(wl.replace(S=int(max(lens))), seed=wl.seed + seed)
+    Kr = [K[b][:, :int(n)] for b, n in enumerate(lens)]
+    Vr = [V[b][:, :int(n)] for b, n in enumerate(lens)]
+    cap = int(max(lens))
+    if paged:
+        table, nblk = W.paged_pool(np.maximum(lens, 1), 64, seed)
+        kp, _ = W.scatter_paged(Kr, [np.zeros((int(n), 0)) for n in lens], table, nblk, 64)
+        vp, _ = W.scatter_paged(Vr, [np.zeros((int(n), 0)) for n in lens], table, nblk, 64)
+        kd, vd, td = S.dev(kp, wl.dtype), S.dev(vp, wl.dtype), torch.tensor(table, device="cuda")
+        shape = gva.make_shape(wl.B, wl.H, wl.G, 64, 64, 0, max_seq_len=cap, block_size=64,
+                               num_blocks=nblk, max_blocks_per_seq=table.shape[1],
+                               split_tokens=split, dtype=wl.dtype)
+    else:
+        kd = S.dev(W.contiguous_cache(Kr, cap, 1), wl.dtype)
+        vd = S.dev(W.contiguous_cache(Vr, cap, 1), wl.dtype)
+        td = None
+        shape = gva.make_shape(wl.B, wl.H, wl.G, 64, 64, 0, capacity=cap, max_seq_len=cap,
+                               split_tokens=split, dtype=wl.dtype)
+    seq = torch.tensor(np.asarray(lens, dtype=np.int32), device="cuda")
+    out = torch.empty(wl.B, wl.H, 64, dtype=W.torch_dtype(wl.dtype), device="cuda")
+    sc = S.gqa_scale(64)
+    print(f"[case] gqa B={wl.B} max_len={cap} paged={paged} split={split}", flush=True)
+    gva.gva_gqa_ref_decode(shape, S.dev(q, wl.dtype), kd, vd, seq, td, sc, out, S.workspace(shape))
+    torch.cuda.synchronize()
+    ref = O.gqa_decode(q, Kr, Vr, lens, sc)
+    return S.host(out), ref
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("lens", [[1, 65, 300], [0, 2, 1000], [4096, 4095]])
+def test_gqa_reference_matches_oracle(paged, lens):
+    wl = _small_wl("bf16", 0, B=len(lens))
+    out, ref = _gqa_run(wl, np.array(lens), paged=paged, split=0 if max(lens) < 1000 else 256)
+    S.assert_close(out, ref, "bf16", f"gqa lens={lens} paged={paged}")
+
+
+def test_gqa_reference_full_wide():
+    """Matched GQA cache of the wide workload (B=32, S=8192, G=4, d_h=64)."""
+    wl = W.WORKLOADS["wide_dr24"].replace(d_r=0)
+    out, ref = _gqa_run(wl, np.full(wl.B, wl.S))
+    S.assert_close(out, ref, "bf16", "gqa full wide")
