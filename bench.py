@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="time eager launches only")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--split", type=int, default=-1,
+                   help="split-K partition length in tokens (-1 = the workload's, 0 = automatic)")
     p.add_argument("--profile-decode", type=int, default=0,
                    help="only run N eager decodes (for rocprofv3 runs) and exit")
     return p.parse_args()
@@ -66,6 +68,8 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     wl = W.WORKLOADS[args.workload]
+    if args.split >= 0:
+        wl = wl.replace(split_tokens=args.split)
     assert not wl.ragged, "bench drives uniform-length workloads"
     base = wl.rope_base
     bpt = gva.gva_cache_bytes_per_token(wl.G, wl.d_v, wl.d_r, wl.dtype)

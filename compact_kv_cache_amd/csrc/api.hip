@@ -2,6 +2,7 @@
 // dispatch to the kernels. Nothing here allocates device memory.
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <cstdlib>
 #include <string>
 
@@ -76,13 +77,14 @@ gva_status check_shape(const gva_shape* s, bool gqa) {
 
 int resolve_split(const gva_shape* s) {
   if (s->split_tokens > 0) return s->split_tokens;
-  // Aim for about 512 workgroups of (sequence, partition, four groups), i.e.
-  // two per compute unit, each streaming whole 64-token tiles.
-  const int64_t base = (int64_t)s->B * ((s->G + 3) / 4);
-  const int64_t want_parts = (512 + base - 1) / base;
+  // About one workgroup of (sequence, group, partition) per compute unit
+  // (256 of them), each partition a whole number of 64-token tiles and at
+  // least one tile per wave of the eight-wave workgroup.
+  const int64_t base = (int64_t)s->B * s->G;
+  const int64_t want_parts = (256 + base - 1) / base;
   const int64_t tiles = (s->max_seq_len + 63) / 64;
   int64_t tiles_per = (tiles + want_parts - 1) / want_parts;
-  if (tiles_per < 1) tiles_per = 1;
+  if (tiles_per < 8) tiles_per = 8;
   return (int)(tiles_per * 64);
 }
 
@@ -199,6 +201,8 @@ gva_status gva_decode(const gva_shape* shape, const void* q_nope, const void* q_
     return fail(GVA_ERR_INVALID_ARGUMENT, "q_rope and kr_cache must be non-NULL when d_r > 0");
   if (shape->block_size != 0 && !block_table)
     return fail(GVA_ERR_INVALID_ARGUMENT, "paged cache needs a block_table");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(GVA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0 (got %g)", (double)scale);
   const size_t need = workspace_for(shape);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
@@ -231,6 +235,8 @@ gva_status gva_gqa_ref_decode(const gva_shape* shape, const void* q, const void*
     return fail(GVA_ERR_INVALID_ARGUMENT, "paged cache needs a block_table");
   if (shape->dtype != GVA_BF16)
     return fail(GVA_ERR_UNSUPPORTED, "GQA reference is built for bf16 caches only");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(GVA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0 (got %g)", (double)scale);
   const size_t need = workspace_for(shape);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,

@@ -1,28 +1,39 @@
 // GVA decode (bf16 cache) on the gfx950 matrix cores, and the same-shape GQA
 // comparison kernel built from the same skeleton.
 //
-// Work split: one workgroup per (sequence b, split-K partition, chunk of four
-// value groups); wave w of the workgroup owns group g = 4*chunk + w and its
-// H/G query heads. Every cache row is read from HBM once per group, never
-// once per head (the GQA tutorial page asks fast kernels to read K/V through
-// the head map instead of copying it per head, section 一次 GQA 计算如何展开).
+// Work split: one workgroup per (sequence b, value group g, token range of
+// split-K partition); its eight waves take interleaved 64-token tiles of the
+// range and merge their softmax states in LDS at the end. Every cache row is
+// read from HBM once per group, never once per head (the GQA tutorial page
+// asks fast kernels to read K/V through the head map instead of copying it per
+// head, section 一次 GQA 计算如何展开). Workgroup ids are mapped so that the G
+// workgroups of one (sequence, range) land on the same XCD and share the
+// positional-key rows k_r through that XCD's L2.
+//
+// Absorption prologue (GVA digest, 方法: Q' = Q M^T; explainer, 正式方案):
+// q'_h = M_h q_nope,h on MFMA (A = rows of M_h, B = q_nope,h in every
+// column), one (head, half of the contraction) per wave; M's rows are visited
+// in a permuted order so the product comes out directly in the score
+// operand's lane layout. M is read once per workgroup; the cache-tile stream
+// starts after the queries are ready.
 //
 // Per wave and 16-token sub-tile, all on v_mfma_f32_16x16x32_bf16:
-//   scores   S^T[tok][col] = V[tok][:] . q'[head(col)][:]   (+ k_r . q_rope)
-//            A operand = V rows exactly as loaded (lane l: token l%16, 8
-//            consecutive channels), B operand = the absorbed queries
-//            q'_h = M_h q_nope,h (GVA digest, 方法; explainer, 正式方案), with
-//            the group's heads repeated across the 16 columns. q' is split
-//            into bf16 hi + lo parts so the score keeps ~16 significant bits.
-//   transpose  C[tok][c] = V[tok][:] . E[:][c] with E a 0/1 selection of 16
-//            channels: produces V^T in the A-operand layout of the next
-//            product, exactly (one nonzero term per output).
-//   P.V      O^T[ch][col] += V^T[ch][tok] . P^T[tok][col] over 32 tokens; the
-//            B operand P^T is the score accumulator itself (same lane layout),
-//            rounded to bf16 after the softmax.
-// Softmax is online (running max / sum per head, exp2 with scale*log2(e)
-// folded into the queries). Long sequences are split into partitions merged
-// by the last workgroup to finish (log-sum-exp), inside this launch.
+//   scores     S^T[tok][col] = V[tok][:] . q'[head(col)][:] + k_r[tok] . q_rope:
+//              A = V rows exactly as loaded (lane l: token l%16, 8 channels),
+//              B = queries with the group's heads repeated across the 16
+//              columns; q' is split into bf16 hi + lo parts.
+//   transpose  C[tok][c] = V[tok][:] . E[:][c], E a 0/1 selection of 16
+//              channels: V^T in the A layout of the next product, exactly.
+//   P.V        O^T[ch][col] += V^T[ch][tok] . P^T[tok][col] over 32 tokens; B =
+//              the score accumulator itself after the softmax, in bf16.
+// Softmax: scores stay unscaled; p = 2^(scale*log2(e)*(s - m_ref)) with one FMA
+// and the raw v_exp_f32. The reference max m_ref only moves when a tile's max
+// exceeds it by more than 2^8 in probability units, so the output rescale is
+// rare and p stays below 256.
+// Cache tiles are read with non-temporal loads from a wave-uniform tile base
+// plus per-lane offsets; rows past the end are clamped, a missing tile reads
+// the first row, so no load is ever predicated and the next tile's loads stay
+// in flight while the current one is computed.
 #include "gva_device.hpp"
 #include "launch.hpp"
 
@@ -31,10 +42,11 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 union Frag {
   bf16x8 v;
-  uint4 u;
+  u32x4 u;
   __bf16 h[8];
 };
 
@@ -42,87 +54,169 @@ __device__ __forceinline__ f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
-
-__device__ __forceinline__ uint4 ld16(const __bf16* p) {
-  return *reinterpret_cast<const uint4*>(p);
+// 16-byte load; `base` is wave-uniform, `off` a per-lane element offset.
+__device__ __forceinline__ u32x4 ld16(const __bf16* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+// Same, for data read exactly once (does not displace resident lines).
+__device__ __forceinline__ u32x4 ld16_stream(const __bf16* base, int off) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
 }
 
-// Per-wave registers for one 64-token tile: 4 sub-tiles of 16 tokens.
-// GVA: score rows = V (sa), positional rows = k_r (kr). GQA: score rows = K
-// (sa), value rows = V (vb). For GVA vb aliases sa.
+constexpr f32x4 kZero4 = {0.f, 0.f, 0.f, 0.f};
+constexpr int kWaves = 8;           // waves per workgroup
+constexpr float kRescaleLog2 = 8.f;  // move the reference max only beyond 2^8
+
+// Registers of one 64-token tile (4 sub-tiles of 16 tokens) for one wave.
+// GVA: sa = V rows, kr = positional keys. GQA: sa = K rows, vb = V rows.
 template <bool GQA, bool DR>
 struct Tile {
-  Frag sa[4][2];  // [sub-tile][channel half]: rows feeding the score product
-  Frag vb[GQA ? 4 : 1][GQA ? 2 : 1];
+  Frag sa[4][2];
+  Frag vb[GQA ? 4 : 1][2];
   Frag kr[DR ? 4 : 1];
+  int t0;     // first token of the tile
+  bool ok;    // tile exists and its page is valid (wave-uniform)
+  bool full;  // all 64 tokens are inside the partition (wave-uniform)
 };
 
 template <int HPG, bool PAGED, bool DR, bool GQA>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeLaunch a) {
+__global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunch a) {
   static_assert(!(GQA && DR), "GQA reference has no positional slice");
-  const int split = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int col = lane & 15, r = lane >> 4;  // MFMA column / lane group
+  constexpr bool QLO = !GQA;  // GQA queries are exact in bf16
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
+  const int col = lane & 15, r = lane >> 4;                 // MFMA column / lane group
   const int H = a.H, G = a.G, d_r = a.d_r;
-  const int g = chunk * 4 + w;
-  const bool active = g < G;
+
+  // Workgroup id -> (sequence, partition) pair p and group g; the G groups of a
+  // pair share id % 8 (one XCD) and have consecutive slots there.
+  const int pairs = a.B * a.n_split;
+  const int q8 = blockIdx.x >> 3;
+  const int g = q8 % G;
+  const int p = (q8 / G) * 8 + (blockIdx.x & 7);
+  if (p >= pairs) return;
+  const int b = p / a.n_split, split = p % a.n_split;
+
   const int n = min(max(a.seq_lens[b], 0), a.max_seq_len);
   const int n_parts = (n + a.split - 1) / a.split;
   if (split >= max(n_parts, 1)) return;  // uniform per workgroup
   const int t_begin = split * a.split;
   const int t_end = min(n, t_begin + a.split);
+  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;  // 0 only when n == 0
   const float sl2 = a.scale * kLog2e;
-  const int jcol = col % HPG;               // head (within group) of this lane's column
-  const int h_col = g * HPG + jcol;         // its global head index
+  const int jcol = col % HPG;        // head (within the group) of this lane's column
+  const int h_col = g * HPG + jcol;  // its global head index
+  // Query preparation: wave w forms head w % HPG over contraction half
+  // (w / HPG) % 2; waves past 2*HPG repeat earlier work and discard it.
+  const int h_w = g * HPG + (w % HPG);
+  const int kc_w = (w / HPG) & 1;
+  const bool q_writer = w < 2 * HPG;
 
-  __shared__ float qsh[4][4][kD];  // [wave][head in group][channel]
+  __shared__ float qsh[2][4][kD];         // [half][head][channel] partial queries
+  __shared__ float red_o[kWaves][4][kD];  // per-wave unnormalized outputs
+  __shared__ float red_ml[kWaves][4][2];  // per-wave (max in log2 units, sum)
 
-  // ---- prologue: queries into B-operand fragments --------------------------
-  Frag qhi[2], qlo[2], qr;
-  if (active) {
-    if (!GQA) {
-      // Absorption: q'_h[d] = sum_j M_h[d][j] q_nope,h[j], lane = d.
-      for (int j = 0; j < HPG; ++j) {
-        const int h = g * HPG + j;
-        const __bf16* Mrow = reinterpret_cast<const __bf16*>(a.M) + ((int64_t)h * kD + lane) * kD;
-        const __bf16* qn = reinterpret_cast<const __bf16*>(a.q_nope) + ((int64_t)b * H + h) * kD;
-        float acc = 0.f;
+  const __bf16* vc = reinterpret_cast<const __bf16*>(a.v_cache);
+  const __bf16* sc = reinterpret_cast<const __bf16*>(GQA ? a.kr_cache : a.v_cache);
+  const __bf16* kc = reinterpret_cast<const __bf16*>(a.kr_cache);
+  const __bf16* qn = reinterpret_cast<const __bf16*>(a.q_nope);
+  const int kr_off = DR ? 8 * min(r, d_r / 8 - 1) : 0;  // lanes past d_r re-read a valid slice
+
+  // ---- prologue loads (issued, and fenced, before any tile load) -------------
+  Frag mA[4], qB;
+  if constexpr (!GQA) {
 #pragma unroll
-        for (int k = 0; k < kD; k += 8) {
-          Frag m8, q8;
-          m8.u = ld16(Mrow + k);
-          q8.u = ld16(qn + k);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc = fmaf((float)m8.h[e], (float)q8.h[e], acc);
-        }
-        qsh[w][j][lane] = acc * sl2;
-      }
-    } else {
-      for (int j = 0; j < HPG; ++j) {
-        const int h = g * HPG + j;
-        qsh[w][j][lane] =
-            (float)reinterpret_cast<const __bf16*>(a.q_nope)[((int64_t)b * H + h) * kD + lane] * sl2;
-      }
+    for (int mb = 0; mb < 4; ++mb) {
+      const int chan = 32 * (mb >> 1) + 8 * (col >> 2) + 4 * (mb & 1) + (col & 3);
+      const __bf16* Mh = reinterpret_cast<const __bf16*>(a.M) + (int64_t)h_w * kD * kD;
+      mA[mb].u = ld16(Mh, chan * kD + 32 * kc_w + 8 * r);
     }
+    qB.u = ld16(qn + ((int64_t)b * H + h_w) * kD, 32 * kc_w + 8 * r);
+  }
+  Frag qr;
+  if constexpr (DR) qr.u = ld16(reinterpret_cast<const __bf16*>(a.q_rope) + ((int64_t)b * H + h_col) * d_r, kr_off);
+  __syncthreads();
+
+  // ---- tile loads ---------------------------------------------------------------
+  auto issue = [&](Tile<GQA, DR>& T, int k) {
+    const int t0 = t_begin + k * kTile;
+    bool ok = k < n_tiles;
+    int64_t vbase = 0, kbase = 0;
+    if constexpr (PAGED) {
+      const int jb = min(t0 / kBlock, a.max_blocks - 1);
+      const int blk = a.block_table[(int64_t)b * a.max_blocks + jb];
+      ok = ok && blk >= 0 && blk < a.num_blocks;
+      vbase = ((int64_t)blk * G + g) * kBlock * kD;
+      kbase = (int64_t)blk * kBlock * d_r;
+    } else {
+      vbase = (((int64_t)b * G + g) * a.capacity + t0) * kD;
+      kbase = ((int64_t)b * a.capacity + t0) * d_r;
+    }
+    if (!ok) vbase = kbase = 0;
+    T.t0 = t0;
+    T.ok = ok;
+    T.full = ok && t0 + kTile <= t_end;
+    // last row this tile may touch: rows past the end re-read it; a missing
+    // tile reads row 0 of the cache
+    const int bound = ok ? min(kTile - 1, t_end - 1 - t0) : 0;
+    const __bf16* vp = sc + vbase;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int row = min(16 * st + col, bound);
+      const int off = row * kD + 8 * r;
+      T.sa[st][0].u = ld16_stream(vp, off);
+      T.sa[st][1].u = ld16_stream(vp, off + 32);
+      if constexpr (GQA) {
+        T.vb[st][0].u = ld16_stream(vc + vbase, off);
+        T.vb[st][1].u = ld16_stream(vc + vbase, off + 32);
+      }
+      if constexpr (DR) T.kr[st].u = ld16_stream(kc + kbase, row * d_r + kr_off);
+    }
+  };
+
+
+  // ---- queries into B-operand fragments ----------------------------------------
+  if constexpr (!GQA) {
+    f32x4 D[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) D[mb] = mma(mA[mb], qB, kZero4);
+    // lane (col 0, group r) holds the half-kc_w partial of q'[32kc + 8r + e]
+    // in D[2kc + e / 4][e % 4]
+    if (q_writer && col == 0) {
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qsh[kc_w][w % HPG][32 * kc2 + 8 * r + e] = D[2 * kc2 + (e >> 2)][e & 3];
+    }
+  } else {
+    if (w < HPG) {
+      qsh[0][w][lane] = (float)qn[((int64_t)b * H + g * HPG + w) * kD + lane];
+      qsh[1][w][lane] = 0.f;
+    }
+  }
+  if constexpr (DR) {
+    if (8 * r >= d_r) qr.u = u32x4{0u, 0u, 0u, 0u};  // slots past d_r contribute nothing
   }
   __syncthreads();
-  if (active) {
+  Frag qhi[2], qlo[2];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+  for (int kc2 = 0; kc2 < 2; ++kc2) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = qsh[w][jcol][32 * kc + 8 * r + e];
-        const __bf16 hi = (__bf16)v;
-        qhi[kc].h[e] = hi;
-        qlo[kc].h[e] = (__bf16)(v - (float)hi);
-      }
-    }
-    if (DR) {
-      const __bf16* q = reinterpret_cast<const __bf16*>(a.q_rope) + ((int64_t)b * H + h_col) * d_r;
-      qr.u = (8 * r < d_r) ? ld16(q + 8 * r) : zero4();
+    for (int e = 0; e < 8; ++e) {
+      const int ch = 32 * kc2 + 8 * r + e;
+      const float v = qsh[0][jcol][ch] + qsh[1][jcol][ch];
+      const __bf16 hi = (__bf16)v;
+      qhi[kc2].h[e] = hi;
+      qlo[kc2].h[e] = (__bf16)(v - (float)hi);
     }
   }
+  // The tile stream starts only now: loads issued earlier would sit between
+  // the prologue's loads and their use (a wave stalls at load issue once the
+  // compute unit's request queues are full).
+  Tile<GQA, DR> X, Y;
+  issue(X, w);
+  issue(Y, w + kWaves);
+
   // Selection fragments: sel[par] picks channel 16*db + col out of the 32
   // channels of half db/2 (par = db % 2).
   Frag sel[2];
@@ -130,66 +224,36 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeLaunch a) {
   for (int par = 0; par < 2; ++par)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      sel[par].h[e] = (__bf16)((r == 2 * par + col / 8 && e == col % 8) ? 1.f : 0.f);
+      sel[par].h[e] = (__bf16)((r == 2 * par + (col >> 3) && e == (col & 7)) ? 1.f : 0.f);
 
-  // ---- streaming loop -------------------------------------------------------
-  const CacheGeom cg{G, d_r, a.capacity, a.num_blocks, a.max_blocks, a.block_table};
-  const __bf16* vc = reinterpret_cast<const __bf16*>(a.v_cache);
-  const __bf16* sc = reinterpret_cast<const __bf16*>(GQA ? a.kr_cache : a.v_cache);
-  const __bf16* kc_ptr = reinterpret_cast<const __bf16*>(a.kr_cache);
-
+  // ---- streaming ------------------------------------------------------------------
   f32x4 acc_o[4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) acc_o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int db = 0; db < 4; ++db) acc_o[db] = kZero4;
+  float m_ref = -INFINITY, l_run = 0.f;  // m_ref in raw score units
+  const float thr = kRescaleLog2 / sl2;
 
-  auto load_tile = [&](Tile<GQA, DR>& T, int t0) {
-    int blk = 0;
-    if (PAGED) blk = page_of(cg, b, t0);
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int tok = t0 + 16 * st + col;
-      const bool ok = active && tok < t_end && (!PAGED || blk >= 0);
-      int64_t vrow, krow = 0;
-      if (PAGED) {
-        vrow = (((int64_t)blk * G + g) * kBlock + (tok % kBlock)) * kD;
-        if (DR) krow = ((int64_t)blk * kBlock + (tok % kBlock)) * d_r;
-      } else {
-        vrow = (((int64_t)b * G + g) * a.capacity + tok) * kD;
-        if (DR) krow = ((int64_t)b * a.capacity + tok) * d_r;
-      }
-      T.sa[st][0].u = ok ? ld16(sc + vrow + 8 * r) : zero4();
-      T.sa[st][1].u = ok ? ld16(sc + vrow + 32 + 8 * r) : zero4();
-      if constexpr (GQA) {
-        T.vb[st][0].u = ok ? ld16(vc + vrow + 8 * r) : zero4();
-        T.vb[st][1].u = ok ? ld16(vc + vrow + 32 + 8 * r) : zero4();
-      }
-      if constexpr (DR) T.kr[st].u = (ok && 8 * r < d_r) ? ld16(kc_ptr + krow + 8 * r) : zero4();
-    }
-  };
-
-  auto process_tile = [&](const Tile<GQA, DR>& T, int t0) {
+  auto process = [&](const Tile<GQA, DR>& T) {
+    if (!T.ok) return;  // wave-uniform
     f32x4 s[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-      c = mma(T.sa[st][0], qhi[0], c);
+      f32x4 c = mma(T.sa[st][0], qhi[0], kZero4);
       c = mma(T.sa[st][1], qhi[1], c);
-      if (!GQA) {
+      if constexpr (QLO) {
         c = mma(T.sa[st][0], qlo[0], c);
         c = mma(T.sa[st][1], qlo[1], c);
       }
-      if constexpr (DR) {
-        const f32x4 cr = mma(T.kr[st], qr, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int i = 0; i < 4; ++i) c[i] = fmaf(cr[i], sl2, c[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (t0 + 16 * st + 4 * r + i >= t_end) c[i] = -INFINITY;
+      if constexpr (DR) c = mma(T.kr[st], qr, c);
       s[st] = c;
     }
-    // online softmax for this lane's head (column)
+    if (!T.full) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (T.t0 + 16 * st + 4 * r + i >= t_end) s[st][i] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int st = 0; st < 4; ++st)
@@ -197,23 +261,24 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeLaunch a) {
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[st][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
+    const float m_new = (mx > m_ref + thr) ? mx : m_ref;
+    if (__any(m_new != m_ref)) {
+      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sl2);  // 0 on the first tile
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc_o[db] *= alpha;
+      m_ref = m_new;
+    }
+    const float bias = -m_ref * sl2;
     float psum = 0.f;
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[st][i] = exp2f(s[st][i] - m_new);
+        s[st][i] = __builtin_amdgcn_exp2f(fmaf(s[st][i], sl2, bias));
         psum += s[st][i];
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) acc_o[db] *= alpha;
-    }
-    // P.V over two 32-token pairs of sub-tiles
+    l_run += psum;
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
       Frag pb;
@@ -226,11 +291,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeLaunch a) {
       for (int db = 0; db < 4; ++db) {
         f32x4 ca, cb;
         if constexpr (GQA) {
-          ca = mma(T.vb[2 * pr][db >> 1], sel[db & 1], f32x4{0.f, 0.f, 0.f, 0.f});
-          cb = mma(T.vb[2 * pr + 1][db >> 1], sel[db & 1], f32x4{0.f, 0.f, 0.f, 0.f});
+          ca = mma(T.vb[2 * pr][db >> 1], sel[db & 1], kZero4);
+          cb = mma(T.vb[2 * pr + 1][db >> 1], sel[db & 1], kZero4);
         } else {
-          ca = mma(T.sa[2 * pr][db >> 1], sel[db & 1], f32x4{0.f, 0.f, 0.f, 0.f});
-          cb = mma(T.sa[2 * pr + 1][db >> 1], sel[db & 1], f32x4{0.f, 0.f, 0.f, 0.f});
+          ca = mma(T.sa[2 * pr][db >> 1], sel[db & 1], kZero4);
+          cb = mma(T.sa[2 * pr + 1][db >> 1], sel[db & 1], kZero4);
         }
         Frag vt;
 #pragma unroll
@@ -243,70 +308,79 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeLaunch a) {
     }
   };
 
-  if (active && t_begin < t_end) {
-    Tile<GQA, DR> A, B;
-    load_tile(A, t_begin);
-    for (int t0 = t_begin; t0 < t_end; t0 += 2 * kTile) {
-      const int t1 = t0 + kTile;
-      if (t1 < t_end) load_tile(B, t1);
-      process_tile(A, t0);
-      if (t1 >= t_end) break;
-      if (t1 + kTile < t_end) load_tile(A, t1 + kTile);
-      process_tile(B, t1);
-    }
+  for (int k = w; k < n_tiles; k += 2 * kWaves) {
+    process(X);
+    issue(X, k + 2 * kWaves);
+    if (k + kWaves >= n_tiles) break;
+    process(Y);
+    issue(Y, k + 3 * kWaves);
   }
 
-  // ---- epilogue ---------------------------------------------------------------
+  // ---- merge the waves ----------------------------------------------------------------
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  __bf16* out = reinterpret_cast<__bf16*>(a.out);
-  const bool writer = active && col < HPG;  // first copy of each head's column
-  if (n_parts <= 1) {
-    if (writer) {
-      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          out[((int64_t)b * H + h_col) * kD + 16 * db + 4 * r + i] = (__bf16)(acc_o[db][i] * inv);
-    }
-    return;
-  }
-  if (writer) {
-    const int64_t slot = ((int64_t)b * H + h_col) * a.n_split + split;
+  if (col < HPG) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a.ws_o[slot * kD + 16 * db + 4 * r + i] = acc_o[db][i];
+      for (int i = 0; i < 4; ++i) red_o[w][col][16 * db + 4 * r + i] = acc_o[db][i];
     if (r == 0) {
-      a.ws_ml[2 * slot] = m_run;
-      a.ws_ml[2 * slot + 1] = l_run;
+      red_ml[w][col][0] = m_ref * sl2;  // log2 units (-inf for a wave without tiles)
+      red_ml[w][col][1] = l_run;
     }
   }
-  int32_t* counter = a.counters + (int64_t)b * gridDim.y + chunk;
-  if (!arrive_last(counter, n_parts)) return;
-  const int heads_here = min(4, G - chunk * 4) * HPG;
-  for (int idx = tid; idx < heads_here * kD; idx += 256) {
-    const int h = chunk * 4 * HPG + idx / kD, d = idx % kD;
-    const int64_t slot0 = ((int64_t)b * H + h) * a.n_split;
-    out[((int64_t)b * H + h) * kD + d] = (__bf16)merge_partials(a.ws_o, a.ws_ml, slot0, n_parts, d);
+  __syncthreads();
+  const int j = tid >> 6, d = lane;  // merge thread: head j (< HPG) of the group, channel d
+  float o = 0.f, l = 0.f, mfin = -INFINITY;
+  if (j < HPG) {
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) mfin = fmaxf(mfin, red_ml[ww][j][0]);
+    if (mfin > -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float f = exp2f(red_ml[ww][j][0] - mfin);
+        o = fmaf(f, red_o[ww][j][d], o);
+        l = fmaf(f, red_ml[ww][j][1], l);
+      }
+    }
   }
+  __bf16* out = reinterpret_cast<__bf16*>(a.out);
+  const int h = g * HPG + j;
+  if (n_parts <= 1) {
+    if (j < HPG) out[((int64_t)b * H + h) * kD + d] = (__bf16)(l > 0.f ? o / l : 0.f);
+    return;
+  }
+  const int64_t slot0 = ((int64_t)b * H + h) * a.n_split;
+  if (j < HPG) {
+    st_dev(a.ws_o + (slot0 + split) * kD + d, o);
+    if (d == 0) {
+      st_dev(a.ws_ml + 2 * (slot0 + split), mfin);
+      st_dev(a.ws_ml + 2 * (slot0 + split) + 1, l);
+    }
+  }
+  int32_t* counter = a.counters + (int64_t)b * G + g;
+  if (!arrive_last(counter, n_parts)) return;
+  if (j < HPG)
+    out[((int64_t)b * H + h) * kD + d] = (__bf16)merge_partials(a.ws_o, a.ws_ml, slot0, n_parts, d);
   if (tid == 0) reset_counter(counter);
 }
 
 template <int HPG, bool DR, bool GQA>
 hipError_t mfma_paged(const DecodeLaunch& a, hipStream_t s) {
-  const dim3 grid(a.n_split, (a.G + 3) / 4, a.B);
+  const int pairs = a.B * a.n_split;
+  const dim3 grid(((pairs + 7) / 8) * 8 * a.G);
   if (a.paged)
-    decode_mfma_kernel<HPG, true, DR, GQA><<<grid, 256, 0, s>>>(a);
+    decode_mfma_kernel<HPG, true, DR, GQA><<<grid, 64 * kWaves, 0, s>>>(a);
   else
-    decode_mfma_kernel<HPG, false, DR, GQA><<<grid, 256, 0, s>>>(a);
+    decode_mfma_kernel<HPG, false, DR, GQA><<<grid, 64 * kWaves, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <int HPG, bool GQA>
 hipError_t mfma_dr(const DecodeLaunch& a, hipStream_t s) {
-  if (!GQA && a.d_r > 0) return mfma_paged<HPG, true, false>(a, s);
+  if constexpr (!GQA) {
+    if (a.d_r > 0) return mfma_paged<HPG, true, false>(a, s);
+  }
   return mfma_paged<HPG, false, GQA>(a, s);
 }
 

@@ -106,10 +106,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeLaunch a) {
   }
   const int64_t slot0 = ((int64_t)b * H + h) * a.n_split;
   if (w < HPG) {
-    a.ws_o[(slot0 + split) * kD + lane] = o;
+    st_dev(a.ws_o + (slot0 + split) * kD + lane, o);
     if (lane == 0) {
-      a.ws_ml[2 * (slot0 + split)] = m;
-      a.ws_ml[2 * (slot0 + split) + 1] = l;
+      st_dev(a.ws_ml + 2 * (slot0 + split), m);
+      st_dev(a.ws_ml + 2 * (slot0 + split) + 1, l);
     }
   }
   int32_t* counter = a.counters + (int64_t)b * a.G + g;

@@ -103,24 +103,35 @@ __device__ __forceinline__ int64_t kr_row(const CacheGeom& c, int b, int t) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K arrival: every workgroup of one (sequence, group) publishes its
-// partial result, then bumps an arrival counter; the one that arrives last
-// merges all partials and resets the counter to zero for the next call.
-// Must be reached by every thread of the workgroup. Returns the same value in
-// all threads.
+// Split-K hand-off between workgroups of one (sequence, group chunk).
+// Partials are written and read with device-coherent accesses (relaxed
+// agent-scope atomics: the store writes through, the load misses in the
+// per-XCD caches), so no cache-wide write-back or invalidate is needed. Each
+// workgroup waits until its own partial stores are acknowledged, then bumps
+// the arrival counter; the workgroup that arrives last merges every partial
+// and resets the counter to zero for the next call.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Must be reached by every thread of the workgroup; returns the same value in
+// all of them.
 __device__ __forceinline__ bool arrive_last(int32_t* counter, int n_parts) {
   __shared__ int s_last;
-  __threadfence();  // release: this workgroup's partials are visible device-wide
-  __syncthreads();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();                // ... and so are every other wave's
   if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (old == n_parts - 1);
   }
   __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();  // acquire: every other partial is visible here
-  return last;
+  return s_last != 0;
 }
 
 __device__ __forceinline__ void reset_counter(int32_t* counter) {
@@ -129,16 +140,37 @@ __device__ __forceinline__ void reset_counter(int32_t* counter) {
 
 // Log-sum-exp merge of n_parts partials of one head for channel d:
 // out = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s, M = max_s m_s, with
-// m_s in log2 units and o_s unnormalized.
+// m_s in log2 units and o_s unnormalized. Partials are fetched eight at a
+// time with all loads in flight together, merged online across batches.
 __device__ __forceinline__ float merge_partials(const float* o, const float* ml, int64_t slot0,
                                                 int n_parts, int d) {
-  float M = -INFINITY;
-  for (int s = 0; s < n_parts; ++s) M = fmaxf(M, ml[2 * (slot0 + s)]);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < n_parts; ++s) {
-    const float w = exp2f(ml[2 * (slot0 + s)] - M);
-    num = fmaf(w, o[(slot0 + s) * kD + d], num);
-    den = fmaf(w, ml[2 * (slot0 + s) + 1], den);
+  constexpr int K = 8;
+  float M = -INFINITY, num = 0.f, den = 0.f;
+  for (int base = 0; base < n_parts; base += K) {
+    float mv[K], lv[K], ov[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const int64_t s = slot0 + min(base + i, n_parts - 1);
+      mv[i] = ld_dev(ml + 2 * s);
+      lv[i] = ld_dev(ml + 2 * s + 1);
+      ov[i] = ld_dev(o + s * kD + d);
+    }
+    float bm = M;
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+      if (base + i < n_parts) bm = fmaxf(bm, mv[i]);
+    const float rescale = exp2f(M - bm);  // 0 before the first batch
+    num *= rescale;
+    den *= rescale;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      if (base + i < n_parts) {
+        const float w = exp2f(mv[i] - bm);
+        num = fmaf(w, ov[i], num);
+        den = fmaf(w, lv[i], den);
+      }
+    }
+    M = bm;
   }
   return den > 0.f ? num / den : 0.f;
 }

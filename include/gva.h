@@ -151,7 +151,7 @@ gva_status gva_rope_query(const gva_shape* shape, const void* q_rope_in, void* q
  *   M        [H][d_v][d_n]    reconstruction maps (K_h = V_g(h) M_h)
  *   v_cache, kr_cache, block_table   as described at gva_shape
  *   seq_lens int32 [B]        tokens to attend (the query's own included)
- *   scale    softmax scale (e.g. 1/sqrt(d_n + d_r))
+ *   scale    softmax scale, finite and > 0 (e.g. 1/sqrt(d_n + d_r))
  *   out      [B][H][d_v]      call dtype; rows with seq_lens[b] <= 0 are zero
  *   workspace, workspace_bytes   device scratch of at least
  *            gva_decode_workspace_bytes(shape) bytes (may be NULL/0 when that

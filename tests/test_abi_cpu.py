@@ -117,6 +117,14 @@ def test_decode_rejects_missing_pointers_and_workspace():
                               None) == _lib.GVA_ERR_INVALID_ARGUMENT
 
 
+def test_decode_rejects_bad_scale():
+    s = _shape()
+    for bad in (0.0, -0.5, float("inf"), float("nan")):
+        st = gva.lib.gva_decode(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, bad, FAKE, FAKE, 1 << 30,
+                                None)
+        assert st == _lib.GVA_ERR_INVALID_ARGUMENT
+
+
 def test_append_and_rope_query_reject_bad_arguments():
     s = _shape()
     L = gva.lib
