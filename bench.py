@@ -87,7 +87,7 @@ def main():
     kr_new = W.round_storage(rng.standard_normal((total_steps, wl.B, 1, wl.d_r)), wl.dtype)
     td = W.torch_dtype(wl.dtype)
     to = lambda x: W.to_torch(x, wl.dtype).to(dev)  # noqa: E731
-    q_nope, q_rope, M = to(inp.q_nope), to(inp.q_rope), to(inp.M)
+    q_nope, q_rope, M0 = to(inp.q_nope), to(inp.q_rope), to(inp.M)
     v_new_d, kr_new_d = to(v_new), to(kr_new)
     q_rot = torch.empty_like(q_rope)
     out = torch.empty(wl.B, wl.H, wl.d_v, dtype=td, device=dev)
@@ -105,6 +105,8 @@ def main():
         c.seq_lens.copy_(first.seq_lens)
         caches.append(c)
     del inp
+    # every replica stands for one layer and carries its own reconstruction maps
+    Ms = [M0] + [M0.clone() for _ in range(R - 1)]
     n_host = [wl.S] * R
     ws_bytes = max(gva.gva_decode_workspace_bytes(caches[0].shape(n, wl.split_tokens))
                    for n in range(wl.S, cap + 1))
@@ -116,7 +118,7 @@ def main():
 
     def decode(r):
         c = caches[r]
-        gva.gva_decode(shape_at(r, n_host[r]), q_nope, q_rot, M, c.v_cache, c.kr_cache,
+        gva.gva_decode(shape_at(r, n_host[r]), q_nope, q_rot, Ms[r], c.v_cache, c.kr_cache,
                        c.seq_lens, None, wl.scale, out, ws)
 
     step_bytes = []
@@ -189,9 +191,11 @@ def main():
     dec_ms = [a.elapsed_time(b) for a, b in evs]
     dec_ms_mean = float(np.mean(dec_ms))
     dec_bytes_mean = float(np.mean(dec_bytes))
-    achieved = dec_bytes_mean / (dec_ms_mean * 1e-3) / 1e9
 
-    # back-to-back decodes in one graph (kernel time + launch gaps)
+    # ---- timed region 3: K decode launches back to back (one graph), HIP
+    # events around the whole run on the launch stream: the average launch
+    # duration without per-call event overhead (this is the figure the
+    # kernel trace's average reproduces)
     ms_dec_graph = None
     if use_graph:
         g2 = torch.cuda.CUDAGraph()
@@ -205,6 +209,8 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ms_dec_graph = e0.elapsed_time(e1) / K
+    ms_launch = ms_dec_graph if ms_dec_graph is not None else dec_ms_mean
+    achieved = dec_bytes_mean / (ms_launch * 1e-3) / 1e9
 
     traffic = None  # filled from profiles only while the kernel source matches (see design doc)
 
@@ -228,8 +234,8 @@ def main():
                    "replicas": R, "split_tokens": gva.gva_decode_split_tokens(shape_at(0, wl.S)),
                    "graph": use_graph},
         "cache_read_GBps": round(mean_step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "decode_us": round(dec_ms_mean * 1e3, 3),
-        "decode_graph_us": None if ms_dec_graph is None else round(ms_dec_graph * 1e3, 3),
+        "decode_us": round(ms_launch * 1e3, 3),
+        "decode_event_per_call_us": round(dec_ms_mean * 1e3, 3),
         "eager_ms_per_step": round(ms_eager, 6),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -260,7 +266,7 @@ def cpu_baseline(wl, seconds: float):
                           wl.rope_base, wl.dtype)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds or reps >= 50:
+        if el >= seconds or reps >= 1000:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": round(reps / el, 4), "unit": "steps/s", "cores": int(threads),
