@@ -2,9 +2,11 @@
 """GVA decode benchmark on one MI355X.
 
 A step is one pass of the decode hot path for one layer's compact cache:
-gva_append (one new token per sequence, RoPE on its positional key), then
-gva_rope_query (rotate the query's positional slice), then gva_decode
-(absorbed scores over V and k_r, online softmax, P.V, split-K merge).
+append one new token per sequence (RoPE on its positional key), rotate the
+query's positional slice, decode (absorbed scores over V and k_r, online
+softmax, P.V, split-K merge). The headline runs it as gva_decode_step (one
+launch); the same step as three calls (gva_append, gva_rope_query,
+gva_decode) is reported beside it.
 Consecutive steps visit R distinct cache replicas (layers) so every decode
 reads data that has not been touched for more than the 256 MB last-level
 cache; the default workload is B=16, S=4096, H=16, G=4, d_v=d_n=64, d_r=16,
@@ -76,7 +78,7 @@ def main():
     cache_bytes = wl.B * wl.S * bpt
     R = args.replicas or max(2, math.ceil(512e6 / cache_bytes))
     K, Wm = args.steps, args.warmup
-    total_steps = Wm + 3 * K + 8
+    total_steps = Wm + 4 * K + 8
     per_rep = math.ceil(total_steps / R) + 1
     cap = wl.S + per_rep
 
@@ -122,6 +124,18 @@ def main():
                        c.seq_lens, None, wl.scale, out, ws)
 
     step_bytes = []
+    ws_step_bytes = max(gva.gva_decode_step_workspace_bytes(caches[0].shape(n, wl.split_tokens))
+                        for n in range(wl.S, cap + 1))
+    ws_step = torch.zeros(ws_step_bytes // 4 + 1, dtype=torch.float32, device=dev)
+
+    def fused_step(i):
+        r = i % R
+        c = caches[r]
+        n_host[r] += 1
+        gva.gva_decode_step(shape_at(r, n_host[r]), v_new_d[i].view(wl.B, wl.G, wl.d_v),
+                            kr_new_d[i].view(wl.B, wl.d_r), q_nope, q_rope, Ms[r], c.v_cache,
+                            c.kr_cache, c.seq_lens, None, wl.scale, base, out, ws_step)
+        step_bytes.append(wl.B * n_host[r] * bpt)
 
     def step(i):
         r = i % R
@@ -141,39 +155,51 @@ def main():
         return
 
     i_step = 0
-    for _ in range(Wm):
-        step(i_step)
+    for k in range(Wm):  # warm both forms of the step
+        (fused_step if k % 2 == 0 else step)(i_step)
         i_step += 1
     torch.cuda.synchronize()
 
-    # ---- timed region 1: whole step (append + rope_query + decode) ---------
-    use_graph = not args.no_graph
-    step_bytes.clear()
-    if use_graph:
+    def graph_time(fn, first):
+        """Capture K calls of fn into one graph, replay once between events."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for _ in range(K):
-                step(i_step)
-                i_step += 1
+            for k in range(K):
+                fn(first + k)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         g.replay()
         e1.record()
         torch.cuda.synchronize()
-        ms_graph = e0.elapsed_time(e1) / K
+        return e0.elapsed_time(e1) / K
+
+    # ---- timed region 1: the whole step, one launch (gva_decode_step) --------
+    use_graph = not args.no_graph
+    step_bytes.clear()
+    if use_graph:
+        ms_step = graph_time(fused_step, i_step)
     else:
-        ms_graph = None
-    # eager timing of the same step sequence (host launch overhead included)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(K):
+            fused_step(i_step + k)
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / K
+    i_step += K
+    mean_step_bytes = float(np.mean(step_bytes))
+    # the same step as three calls (append, rope_query, decode)
+    ms_three = graph_time(step, i_step) if use_graph else None
+    i_step += K if use_graph else 0
+    # eager (host-launched) fused steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(K):
-        step(i_step)
-        i_step += 1
+    for k in range(K):
+        fused_step(i_step + k)
     torch.cuda.synchronize()
     ms_eager = (time.perf_counter() - t0) * 1e3 / K
-    ms_per_step = ms_graph if ms_graph is not None else ms_eager
-    mean_step_bytes = float(np.mean(step_bytes))
+    i_step += K
+    ms_per_step = ms_step
 
     # ---- timed region 2: decode kernel alone, HIP events around each call --
     stream = torch.cuda.current_stream()
@@ -232,11 +258,12 @@ def main():
                                f"contiguous cache, {R} cold replicas",
                    "B": wl.B, "S": wl.S, "H": wl.H, "G": wl.G, "d_v": wl.d_v, "d_r": wl.d_r,
                    "replicas": R, "split_tokens": gva.gva_decode_split_tokens(shape_at(0, wl.S)),
-                   "graph": use_graph},
+                   "graph": use_graph, "step": "gva_decode_step (one launch)"},
         "cache_read_GBps": round(mean_step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "decode_us": round(ms_launch * 1e3, 3),
         "decode_event_per_call_us": round(dec_ms_mean * 1e3, 3),
         "eager_ms_per_step": round(ms_eager, 6),
+        "three_call_steps_per_s": None if ms_three is None else round(1e3 / ms_three, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,

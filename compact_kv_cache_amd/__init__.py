@@ -16,8 +16,8 @@ from ._lib import GVA_BF16, GVA_F32, GvaShape
 
 __all__ = [
     "GvaShape", "GVA_F32", "GVA_BF16", "GvaError", "make_shape", "lib",
-    "gva_append", "gva_rope_query", "gva_decode", "gva_gqa_ref_decode",
-    "gva_decode_workspace_bytes", "gva_decode_split_tokens", "gva_cache_bytes_per_token",
+    "gva_append", "gva_rope_query", "gva_decode", "gva_decode_step", "gva_gqa_ref_decode",
+    "gva_decode_workspace_bytes", "gva_decode_step_workspace_bytes", "gva_decode_split_tokens", "gva_cache_bytes_per_token",
     "gva_status_string", "gva_abi_version", "workspace_for",
 ]
 
@@ -98,6 +98,21 @@ def gva_decode(shape: GvaShape, q_nope, q_rope, M, v_cache, kr_cache, seq_lens, 
                           _stream(stream)), "gva_decode")
 
 
+def gva_decode_step(shape: GvaShape, v_new, kr_new, q_nope, q_rope, M, v_cache, kr_cache, seq_lens,
+                    block_table, scale: float, rope_base: float, out, workspace, stream=None) -> None:
+    dt = _TORCH.get(shape.dtype)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gva_decode_step(shape, _ptr(v_new, dt, "v_new"), _ptr(kr_new, dt, "kr_new"),
+                               _ptr(q_nope, dt, "q_nope"), _ptr(q_rope, dt, "q_rope"),
+                               _ptr(M, dt, "M"), _ptr(v_cache, dt, "v_cache"),
+                               _ptr(kr_cache, dt, "kr_cache"),
+                               _ptr(seq_lens, torch.int32, "seq_lens"),
+                               _ptr(block_table, torch.int32, "block_table"), float(scale),
+                               float(rope_base), _ptr(out, dt, "out"),
+                               _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream)),
+           "gva_decode_step")
+
+
 def gva_gqa_ref_decode(shape: GvaShape, q, k_cache, v_cache, seq_lens, block_table, scale: float,
                        out, workspace=None, stream=None) -> None:
     dt = _TORCH.get(shape.dtype)
@@ -112,6 +127,10 @@ def gva_gqa_ref_decode(shape: GvaShape, q, k_cache, v_cache, seq_lens, block_tab
 
 def gva_decode_workspace_bytes(shape: GvaShape) -> int:
     return int(lib.gva_decode_workspace_bytes(shape))
+
+
+def gva_decode_step_workspace_bytes(shape: GvaShape) -> int:
+    return int(lib.gva_decode_step_workspace_bytes(shape))
 
 
 def gva_decode_split_tokens(shape: GvaShape) -> int:

@@ -1,7 +1,8 @@
 """Compile the HIP sources of the GVA library into libgva.so (gfx950).
 
-Run as `python -m compact_kv_cache_amd._build` or through
-`__graft_entry__.build()`. Every call recompiles; objects go to
+Run as `python compact_kv_cache_amd/_build.py` or through
+`__graft_entry__.build()` (both load this file without importing the package,
+whose import needs the library). Every call recompiles; objects go to
 compact_kv_cache_amd/_build/, the library next to this file.
 """
 from __future__ import annotations

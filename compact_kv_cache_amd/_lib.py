@@ -42,6 +42,9 @@ SIGNATURES = {
     "gva_rope_query": (ctypes.c_int, [_shp, _vp, _vp, _vp, ctypes.c_float, _vp]),
     "gva_decode": (ctypes.c_int, [_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                   _vp, ctypes.c_size_t, _vp]),
+    "gva_decode_step": (ctypes.c_int, [_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       ctypes.c_float, ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]),
+    "gva_decode_step_workspace_bytes": (ctypes.c_size_t, [_shp]),
     "gva_gqa_ref_decode": (ctypes.c_int, [_shp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp,
                                           ctypes.c_size_t, _vp]),
     "gva_decode_workspace_bytes": (ctypes.c_size_t, [_shp]),

@@ -10,7 +10,8 @@ from typing import Optional
 
 import torch
 
-from . import GvaShape, gva_append, gva_decode, gva_decode_workspace_bytes, make_shape
+from . import (GvaShape, gva_append, gva_decode, gva_decode_step, gva_decode_step_workspace_bytes,
+               gva_decode_workspace_bytes, make_shape)
 
 _TD = {"bf16": torch.bfloat16, "f32": torch.float32}
 
@@ -90,3 +91,18 @@ class GvaCache:
             workspace = self.workspace(max_seq_len, split_tokens)
         gva_decode(shape, q_nope, q_rope, M, self.v_cache, self.kr_cache, self.seq_lens,
                    self.block_table, scale, out, workspace, stream)
+
+    def step_workspace(self, max_seq_len: int, split_tokens: int = 0) -> torch.Tensor:
+        n = gva_decode_step_workspace_bytes(self.shape(max_seq_len, split_tokens))
+        return torch.zeros((n + 3) // 4, dtype=torch.float32, device=self.v_cache.device)
+
+    def step(self, v_new, kr_new, q_nope, q_rope, M, scale: float, out, max_seq_len: int,
+             split_tokens: int = 0, workspace=None, rope_base: float = 10000.0, stream=None) -> None:
+        """One fused decode step: append v_new [B, G, d_v] / pre-RoPE kr_new [B, d_r],
+        rotate pre-RoPE q_rope, decode into out. max_seq_len bounds the lengths
+        after the append."""
+        shape = self.shape(max_seq_len, split_tokens)
+        if workspace is None:
+            workspace = self.step_workspace(max_seq_len, split_tokens)
+        gva_decode_step(shape, v_new, kr_new, q_nope, q_rope, M, self.v_cache, self.kr_cache,
+                        self.seq_lens, self.block_table, scale, rope_base, out, workspace, stream)

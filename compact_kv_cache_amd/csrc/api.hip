@@ -98,11 +98,17 @@ size_t workspace_for(const gva_shape* s) {
 }
 
 void set_workspace(gva::DecodeLaunch& a, void* workspace) {
-  if (a.n_split <= 1 || !workspace) return;
+  if (!workspace) return;
   char* base = static_cast<char*>(workspace);
   a.counters = reinterpret_cast<int32_t*>(base);
+  a.counters_seq = a.counters + (size_t)a.B * a.G;
   a.ws_o = reinterpret_cast<float*>(base + gva::ws_counter_bytes(a.B, a.G));
   a.ws_ml = a.ws_o + (size_t)a.B * a.H * a.n_split * 64;
+}
+
+size_t step_workspace_for(const gva_shape* s) {
+  const int split = resolve_split(s);
+  return gva::ws_step_bytes(s->B, s->H, s->G, n_splits(s, split));
 }
 
 // GVA_FORCE_VALU=1 routes bf16 decodes to the vector-ALU kernel (used to
@@ -165,7 +171,7 @@ gva_status gva_append(const gva_shape* shape, const void* v_new, const void* kr_
   a.v_cache = v_cache;
   a.kr_cache = kr_cache;
   a.block_table = block_table;
-  a.rope_base = rope_base;
+  a.rope = gva::make_rope_table(rope_base, shape->d_r);
   return hip_status(gva::launch_append(a, stream), "gva_append launch");
 }
 
@@ -185,7 +191,7 @@ gva_status gva_rope_query(const gva_shape* shape, const void* q_rope_in, void* q
   a.q_in = q_rope_in;
   a.q_out = q_rope_out;
   a.seq_lens = seq_lens;
-  a.rope_base = rope_base;
+  a.rope = gva::make_rope_table(rope_base, shape->d_r);
   return hip_status(gva::launch_rope_query(a, stream), "gva_rope_query launch");
 }
 
@@ -221,6 +227,107 @@ gva_status gva_decode(const gva_shape* shape, const void* q_nope, const void* q_
   const hipError_t e = (a.bf16 && !force_valu()) ? gva::launch_decode_mfma(a, stream)
                                                  : gva::launch_decode_valu(a, stream);
   return hip_status(e, "gva_decode launch");
+}
+
+gva_status gva_decode_step(const gva_shape* shape, const void* v_new, const void* kr_new,
+                           const void* q_nope, const void* q_rope, const void* M, void* v_cache,
+                           void* kr_cache, int32_t* seq_lens, const int32_t* block_table, float scale,
+                           float rope_base, void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  gva_status st = check_shape(shape, false);
+  if (st != GVA_OK) return st;
+  if (!v_new || !q_nope || !M || !v_cache || !seq_lens || !out)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "v_new, q_nope, M, v_cache, seq_lens and out must be non-NULL");
+  if (shape->d_r > 0 && (!kr_new || !q_rope || !kr_cache))
+    return fail(GVA_ERR_INVALID_ARGUMENT, "kr_new, q_rope and kr_cache must be non-NULL when d_r > 0");
+  if (shape->block_size != 0 && !block_table)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "paged cache needs a block_table");
+  if (shape->max_seq_len < 1)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "max_seq_len must bound the length after the append (>= 1)");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(GVA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0 (got %g)", (double)scale);
+  if (!(rope_base > 0.f)) return fail(GVA_ERR_INVALID_ARGUMENT, "rope_base must be > 0");
+  const size_t need = step_workspace_for(shape);
+  if (!workspace || workspace_bytes < need)
+    return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  const bool paged = shape->block_size != 0;
+  const int cap_tokens = paged ? shape->max_blocks_per_seq * 64 : shape->capacity;
+  if (shape->dtype == GVA_BF16 && !force_valu()) {
+    gva::DecodeLaunch a = make_decode(shape);
+    a.q_nope = q_nope;
+    a.q_rope = q_rope;
+    a.M = M;
+    a.v_cache = v_cache;
+    a.kr_cache = kr_cache;
+    a.seq_lens = seq_lens;
+    a.block_table = block_table;
+    a.scale = scale;
+    a.out = out;
+    set_workspace(a, workspace);
+    a.step = true;
+    a.cap_tokens = cap_tokens;
+    a.seq_lens_rw = seq_lens;
+    a.v_cache_rw = v_cache;
+    a.kr_cache_rw = kr_cache;
+    a.v_new = v_new;
+    a.kr_new = kr_new;
+    a.rope = gva::make_rope_table(rope_base, shape->d_r);
+    return hip_status(gva::launch_step_mfma(a, stream), "gva_decode_step launch");
+  }
+  // fp32 (or forced vector-ALU path): the three kernels in sequence; the
+  // rotated query goes to the scratch area at the end of the workspace.
+  void* q_rot = static_cast<char*>(workspace) + need - gva::ws_qrot_bytes(shape->B, shape->H);
+  gva::AppendLaunch ap{};
+  ap.B = shape->B;
+  ap.G = shape->G;
+  ap.d_r = shape->d_r;
+  ap.n_new = 1;
+  ap.capacity = shape->capacity;
+  ap.num_blocks = shape->num_blocks;
+  ap.max_blocks = shape->max_blocks_per_seq;
+  ap.paged = paged;
+  ap.bf16 = shape->dtype == GVA_BF16;
+  ap.v_new = v_new;
+  ap.kr_new = kr_new;
+  ap.seq_lens = seq_lens;
+  ap.v_cache = v_cache;
+  ap.kr_cache = kr_cache;
+  ap.block_table = block_table;
+  ap.rope = gva::make_rope_table(rope_base, shape->d_r);
+  hipError_t e = gva::launch_append(ap, stream);
+  if (e == hipSuccess && shape->d_r > 0) {
+    gva::RopeQueryLaunch rq{};
+    rq.B = shape->B;
+    rq.H = shape->H;
+    rq.d_r = shape->d_r;
+    rq.bf16 = ap.bf16;
+    rq.q_in = q_rope;
+    rq.q_out = q_rot;
+    rq.seq_lens = seq_lens;
+    rq.rope = gva::make_rope_table(rope_base, shape->d_r);
+    e = gva::launch_rope_query(rq, stream);
+  }
+  if (e == hipSuccess) {
+    gva::DecodeLaunch a = make_decode(shape);
+    a.q_nope = q_nope;
+    a.q_rope = shape->d_r > 0 ? q_rot : nullptr;
+    a.M = M;
+    a.v_cache = v_cache;
+    a.kr_cache = kr_cache;
+    a.seq_lens = seq_lens;
+    a.block_table = block_table;
+    a.scale = scale;
+    a.out = out;
+    set_workspace(a, workspace);
+    e = gva::launch_decode_valu(a, stream);
+  }
+  return hip_status(e, "gva_decode_step launch");
+}
+
+size_t gva_decode_step_workspace_bytes(const gva_shape* shape) {
+  if (check_shape(shape, false) != GVA_OK) return 0;
+  return step_workspace_for(shape);
 }
 
 gva_status gva_gqa_ref_decode(const gva_shape* shape, const void* q, const void* k_cache,

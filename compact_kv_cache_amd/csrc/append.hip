@@ -50,8 +50,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendLaunch a, CacheGeom c
       if (dst < 0) continue;
       const int64_t src = ((int64_t)b * a.n_new + t) * a.d_r + 2 * p;
       double y0, y1;
-      rope_pair((double)to_f32(ksrc[src]), (double)to_f32(ksrc[src + 1]), (double)pos, p, a.d_r,
-                a.rope_base, y0, y1);
+      rope_pair((double)to_f32(ksrc[src]), (double)to_f32(ksrc[src + 1]), (double)pos, a.rope.theta[p],
+                y0, y1);
       kdst[dst + 2 * p] = from_f64<T>(y0);
       kdst[dst + 2 * p + 1] = from_f64<T>(y1);
     }
@@ -79,8 +79,7 @@ __global__ __launch_bounds__(256) void rope_query_kernel(RopeQueryLaunch a) {
     const int h = i / half, p = i % half;
     const int64_t off = ((int64_t)b * a.H + h) * a.d_r + 2 * p;
     double y0, y1;
-    rope_pair((double)to_f32(src[off]), (double)to_f32(src[off + 1]), pos, p, a.d_r,
-              a.rope_base, y0, y1);
+    rope_pair((double)to_f32(src[off]), (double)to_f32(src[off + 1]), pos, a.rope.theta[p], y0, y1);
     dst[off] = from_f64<T>(y0);
     dst[off + 1] = from_f64<T>(y1);
   }

@@ -1,5 +1,6 @@
-// GVA decode (bf16 cache) on the gfx950 matrix cores, and the same-shape GQA
-// comparison kernel built from the same skeleton.
+// GVA decode (bf16 cache) on the gfx950 matrix cores, the fused decode step
+// (append one token + rotate the query + decode, one launch), and the
+// same-shape GQA comparison kernel, all from one skeleton.
 //
 // Work split: one workgroup per (sequence b, value group g, token range of
 // split-K partition); its eight waves take interleaved 64-token tiles of the
@@ -14,8 +15,8 @@
 // q'_h = M_h q_nope,h on MFMA (A = rows of M_h, B = q_nope,h in every
 // column), one (head, half of the contraction) per wave; M's rows are visited
 // in a permuted order so the product comes out directly in the score
-// operand's lane layout. M is read once per workgroup; the cache-tile stream
-// starts after the queries are ready.
+// operand's lane layout. M is read once per workgroup; waves without a query
+// to prepare start the cache-tile stream meanwhile.
 //
 // Per wave and 16-token sub-tile, all on v_mfma_f32_16x16x32_bf16:
 //   scores     S^T[tok][col] = V[tok][:] . q'[head(col)][:] + k_r[tok] . q_rope:
@@ -34,6 +35,17 @@
 // plus per-lane offsets; rows past the end are clamped, a missing tile reads
 // the first row, so no load is ever predicated and the next tile's loads stay
 // in flight while the current one is computed.
+//
+// Fused step (the decode loop of the GQA tutorial page, section on cache
+// growth: store the new token's state, then let its query read the cache up to
+// and including itself): the appended position is the old seq_lens[b]; the
+// positional key and the query slice are rotated in the prologue with the same
+// double-precision routine as gva_append / gva_rope_query, split-0 workgroups
+// store the new rows, and the workgroup whose tile holds the new position
+// substitutes that row in registers. Every workgroup of the sequence takes a
+// ticket after reading seq_lens[b]; the last ticket stores the new length, so
+// no workgroup can observe it mid-call. Results equal the three separate
+// calls bit for bit.
 #include "gva_device.hpp"
 #include "launch.hpp"
 
@@ -64,7 +76,7 @@ __device__ __forceinline__ u32x4 ld16_stream(const __bf16* base, int off) {
 }
 
 constexpr f32x4 kZero4 = {0.f, 0.f, 0.f, 0.f};
-constexpr int kWaves = 8;           // waves per workgroup
+constexpr int kWaves = 8;            // waves per workgroup
 constexpr float kRescaleLog2 = 8.f;  // move the reference max only beyond 2^8
 
 // Registers of one 64-token tile (4 sub-tiles of 16 tokens) for one wave.
@@ -75,13 +87,15 @@ struct Tile {
   Frag vb[GQA ? 4 : 1][2];
   Frag kr[DR ? 4 : 1];
   int t0;     // first token of the tile
+  int bound;  // last row of the tile that was read (rows past it re-read it)
   bool ok;    // tile exists and its page is valid (wave-uniform)
   bool full;  // all 64 tokens are inside the partition (wave-uniform)
 };
 
-template <int HPG, bool PAGED, bool DR, bool GQA>
+template <int HPG, bool PAGED, bool DR, bool GQA, bool STEP>
 __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunch a) {
   static_assert(!(GQA && DR), "GQA reference has no positional slice");
+  static_assert(!(GQA && STEP), "the fused step is GVA only");
   constexpr bool QLO = !GQA;  // GQA queries are exact in bf16
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
@@ -97,24 +111,61 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   if (p >= pairs) return;
   const int b = p / a.n_split, split = p % a.n_split;
 
-  const int n = min(max(a.seq_lens[b], 0), a.max_seq_len);
+  // Sequence length. Fused step: the token appended by this call sits at
+  // position `pos` (the stored length) unless the cache is full.
+  const int stored = max(a.seq_lens[b], 0);
+  int pos = 0, n_full = stored;
+  bool has_new = false;
+  if constexpr (STEP) {
+    pos = stored;
+    has_new = pos < a.cap_tokens;
+    n_full = has_new ? pos + 1 : a.cap_tokens;
+  }
+  const int n = min(n_full, a.max_seq_len);
   const int n_parts = (n + a.split - 1) / a.split;
-  if (split >= max(n_parts, 1)) return;  // uniform per workgroup
+
+  // Fused step: a workgroup takes its ticket only after a barrier that
+  // follows every wave's read of seq_lens[b] (the barrier waits for the scalar
+  // read to return). The last of the sequence's G * n_split tickets stores the
+  // new length, which therefore cannot be observed by any workgroup of this
+  // call. Participating workgroups take the ticket just before their tile
+  // stream, so its round trip hides under the tile loads.
+  int ticket = 0;
+  auto take_ticket = [&]() {
+    if (tid == 0)
+      ticket = __hip_atomic_fetch_add(a.counters_seq + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto finish_step = [&]() {
+    if constexpr (STEP) {
+      if (tid == 0 && ticket == G * a.n_split - 1) {
+        a.seq_lens_rw[b] = n_full;
+        __hip_atomic_store(a.counters_seq + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  };
+  if (split >= max(n_parts, 1)) {  // uniform per workgroup
+    if constexpr (STEP) {
+      __syncthreads();
+      take_ticket();
+      finish_step();
+    }
+    return;
+  }
   const int t_begin = split * a.split;
   const int t_end = min(n, t_begin + a.split);
   const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;  // 0 only when n == 0
   const float sl2 = a.scale * kLog2e;
   const int jcol = col % HPG;        // head (within the group) of this lane's column
   const int h_col = g * HPG + jcol;  // its global head index
-  // Query preparation: wave w forms head w % HPG over contraction half
-  // (w / HPG) % 2; waves past 2*HPG repeat earlier work and discard it.
-  const int h_w = g * HPG + (w % HPG);
-  const int kc_w = (w / HPG) & 1;
-  const bool q_writer = w < 2 * HPG;
+  // Query preparation: wave w < HPG forms head w of the group; waves 4..7
+  // rotate the fused step's positional slices meanwhile.
+  const int h_w = g * HPG + min(w, HPG - 1);
 
-  __shared__ float qsh[2][4][kD];         // [half][head][channel] partial queries
+  __shared__ float qsh[4][kD];            // [head][channel] absorbed queries
   __shared__ float red_o[kWaves][4][kD];  // per-wave unnormalized outputs
   __shared__ float red_ml[kWaves][4][2];  // per-wave (max in log2 units, sum)
+  __shared__ __bf16 qrot_sh[4][32];       // fused step: rotated query slices
+  __shared__ __bf16 krot_sh[32];          // fused step: rotated appended key
 
   const __bf16* vc = reinterpret_cast<const __bf16*>(a.v_cache);
   const __bf16* sc = reinterpret_cast<const __bf16*>(GQA ? a.kr_cache : a.v_cache);
@@ -122,19 +173,51 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   const __bf16* qn = reinterpret_cast<const __bf16*>(a.q_nope);
   const int kr_off = DR ? 8 * min(r, d_r / 8 - 1) : 0;  // lanes past d_r re-read a valid slice
 
-  // ---- prologue loads (issued, and fenced, before any tile load) -------------
-  Frag mA[4], qB;
+  // ---- prologue loads ------------------------------------------------------------
+  Frag mA[4][2], qB[2];
   if constexpr (!GQA) {
+    if (w < HPG) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int chan = 32 * (mb >> 1) + 8 * (col >> 2) + 4 * (mb & 1) + (col & 3);
-      const __bf16* Mh = reinterpret_cast<const __bf16*>(a.M) + (int64_t)h_w * kD * kD;
-      mA[mb].u = ld16(Mh, chan * kD + 32 * kc_w + 8 * r);
+      for (int mb = 0; mb < 4; ++mb) {
+        const int chan = 32 * (mb >> 1) + 8 * (col >> 2) + 4 * (mb & 1) + (col & 3);
+        const __bf16* Mh = reinterpret_cast<const __bf16*>(a.M) + (int64_t)h_w * kD * kD;
+#pragma unroll
+        for (int kc2 = 0; kc2 < 2; ++kc2) mA[mb][kc2].u = ld16(Mh, chan * kD + 32 * kc2 + 8 * r);
+      }
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) qB[kc2].u = ld16(qn + ((int64_t)b * H + h_w) * kD, 32 * kc2 + 8 * r);
     }
-    qB.u = ld16(qn + ((int64_t)b * H + h_w) * kD, 32 * kc_w + 8 * r);
   }
-  Frag qr;
-  if constexpr (DR) qr.u = ld16(reinterpret_cast<const __bf16*>(a.q_rope) + ((int64_t)b * H + h_col) * d_r, kr_off);
+  Frag qr, vnew[2];
+  if constexpr (DR && !STEP)
+    qr.u = ld16(reinterpret_cast<const __bf16*>(a.q_rope) + ((int64_t)b * H + h_col) * d_r, kr_off);
+  if constexpr (STEP) {
+    const __bf16* vn = reinterpret_cast<const __bf16*>(a.v_new) + ((int64_t)b * G + g) * kD;
+    vnew[0].u = ld16(vn, 8 * r);
+    vnew[1].u = ld16(vn, 32 + 8 * r);
+  }
+  // Fused step: waves 4..7 rotate the group's query slices (pairs
+  // 0 .. HPG*d_r/2-1) and the appended key (the next d_r/2 pairs), exactly as
+  // gva_rope_query and gva_append do; the inputs are loaded here, the rotation
+  // runs after the barrier.
+  const int half = d_r / 2;
+  const int rot_i = (w - 4) * 64 + lane;  // pair handled by this lane (waves 4..7)
+  const bool rot_q = STEP && DR && w >= 4 && rot_i < HPG * half;
+  const bool rot_k = STEP && DR && w >= 4 && !rot_q && rot_i < HPG * half + half;
+  float rx0 = 0.f, rx1 = 0.f;
+  if constexpr (STEP && DR) {
+    if (rot_q) {
+      const int j = rot_i / half, i = rot_i % half;
+      const __bf16* qp = reinterpret_cast<const __bf16*>(a.q_rope) + ((int64_t)b * H + g * HPG + j) * d_r;
+      rx0 = (float)qp[2 * i];
+      rx1 = (float)qp[2 * i + 1];
+    } else if (rot_k) {
+      const int i = rot_i - HPG * half;
+      const __bf16* kn = reinterpret_cast<const __bf16*>(a.kr_new) + (int64_t)b * d_r;
+      rx0 = (float)kn[2 * i];
+      rx1 = (float)kn[2 * i + 1];
+    }
+  }
   __syncthreads();
 
   // ---- tile loads ---------------------------------------------------------------
@@ -159,6 +242,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     // last row this tile may touch: rows past the end re-read it; a missing
     // tile reads row 0 of the cache
     const int bound = ok ? min(kTile - 1, t_end - 1 - t0) : 0;
+    T.bound = bound;
     const __bf16* vp = sc + vbase;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -174,48 +258,111 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     }
   };
 
+  // Waves 4..7 have no query to prepare: they start the tile stream now,
+  // behind the prologue loads already queued (the barrier above orders them).
+  // Waves 0..3 start theirs once the queries are ready.
+  if constexpr (STEP && DR) {
+    if (rot_q) {
+      const int j = rot_i / half, i = rot_i % half;
+      double y0, y1;
+      rope_pair((double)rx0, (double)rx1, (double)max(n_full - 1, 0), a.rope.theta[i], y0, y1);
+      qrot_sh[j][2 * i] = from_f64<__bf16>(y0);
+      qrot_sh[j][2 * i + 1] = from_f64<__bf16>(y1);
+    } else if (rot_k) {
+      const int i = rot_i - HPG * half;
+      double y0, y1;
+      rope_pair((double)rx0, (double)rx1, (double)pos, a.rope.theta[i], y0, y1);
+      krot_sh[2 * i] = from_f64<__bf16>(y0);
+      krot_sh[2 * i + 1] = from_f64<__bf16>(y1);
+    }
+  }
+  Tile<GQA, DR> X, Y;
+  const bool early = w >= 4;
+  if (early) {
+    issue(X, w);
+    issue(Y, w + kWaves);
+  }
 
   // ---- queries into B-operand fragments ----------------------------------------
   if constexpr (!GQA) {
-    f32x4 D[4];
+    if (w < HPG) {
+      f32x4 D[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) D[mb] = mma(mA[mb], qB, kZero4);
-    // lane (col 0, group r) holds the half-kc_w partial of q'[32kc + 8r + e]
-    // in D[2kc + e / 4][e % 4]
-    if (q_writer && col == 0) {
+      for (int mb = 0; mb < 4; ++mb) {
+        D[mb] = mma(mA[mb][0], qB[0], kZero4);
+        D[mb] = mma(mA[mb][1], qB[1], D[mb]);
+      }
+      // lane (col 0, group r) holds q'[32kc + 8r + e] in D[2kc + e / 4][e % 4]
+      if (col == 0) {
 #pragma unroll
-      for (int kc2 = 0; kc2 < 2; ++kc2)
+        for (int kc2 = 0; kc2 < 2; ++kc2)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qsh[kc_w][w % HPG][32 * kc2 + 8 * r + e] = D[2 * kc2 + (e >> 2)][e & 3];
+          for (int e = 0; e < 8; ++e) qsh[w][32 * kc2 + 8 * r + e] = D[2 * kc2 + (e >> 2)][e & 3];
+      }
     }
   } else {
-    if (w < HPG) {
-      qsh[0][w][lane] = (float)qn[((int64_t)b * H + g * HPG + w) * kD + lane];
-      qsh[1][w][lane] = 0.f;
-    }
+    if (w < HPG) qsh[w][lane] = (float)qn[((int64_t)b * H + g * HPG + w) * kD + lane];
   }
-  if constexpr (DR) {
+  if constexpr (DR && !STEP) {
     if (8 * r >= d_r) qr.u = u32x4{0u, 0u, 0u, 0u};  // slots past d_r contribute nothing
   }
   __syncthreads();
-  Frag qhi[2], qlo[2];
+  Frag qhi[2], qlo[2], knew;
 #pragma unroll
   for (int kc2 = 0; kc2 < 2; ++kc2) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int ch = 32 * kc2 + 8 * r + e;
-      const float v = qsh[0][jcol][ch] + qsh[1][jcol][ch];
+      const float v = qsh[jcol][32 * kc2 + 8 * r + e];
       const __bf16 hi = (__bf16)v;
       qhi[kc2].h[e] = hi;
       qlo[kc2].h[e] = (__bf16)(v - (float)hi);
     }
   }
-  // The tile stream starts only now: loads issued earlier would sit between
-  // the prologue's loads and their use (a wave stalls at load issue once the
-  // compute unit's request queues are full).
-  Tile<GQA, DR> X, Y;
-  issue(X, w);
-  issue(Y, w + kWaves);
+  if constexpr (STEP && DR) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qr.h[e] = (8 * r < d_r) ? qrot_sh[jcol][kr_off + e] : (__bf16)0.f;
+      knew.h[e] = krot_sh[kr_off + e];
+    }
+  }
+  // Fused step: split-0 workgroups store the appended token's rows.
+  if constexpr (STEP) {
+    if (split == 0 && has_new && w == 0) {
+      int64_t vrow = -1, krow = -1;
+      if constexpr (PAGED) {
+        const int blk = a.block_table[(int64_t)b * a.max_blocks + pos / kBlock];
+        if (blk >= 0 && blk < a.num_blocks) {
+          vrow = (((int64_t)blk * G + g) * kBlock + pos % kBlock) * kD;
+          krow = ((int64_t)blk * kBlock + pos % kBlock) * d_r;
+        }
+      } else {
+        vrow = (((int64_t)b * G + g) * a.capacity + pos) * kD;
+        krow = ((int64_t)b * a.capacity + pos) * d_r;
+      }
+      if (vrow >= 0) {
+        __bf16* vdst = reinterpret_cast<__bf16*>(a.v_cache_rw) + vrow;
+        const __bf16* vn = reinterpret_cast<const __bf16*>(a.v_new) + ((int64_t)b * G + g) * kD;
+        if (lane < kD / 8) *reinterpret_cast<u32x4*>(vdst + 8 * lane) = ld16(vn, 8 * lane);
+        if constexpr (DR) {
+          if (g == 0 && lane < d_r / 8) {
+            Frag kk;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kk.h[e] = krot_sh[8 * lane + e];
+            *reinterpret_cast<u32x4*>(reinterpret_cast<__bf16*>(a.kr_cache_rw) + krow + 8 * lane) = kk.u;
+          }
+        }
+      }
+    }
+  }
+
+  // Tiles of waves 0..3 are issued only now: issued earlier they would sit
+  // between the prologue's loads and their use (a wave stalls at load issue
+  // once the compute unit's request queues are full).
+  if constexpr (STEP) take_ticket();
+  if (!early) {
+    issue(X, w);
+    issue(Y, w + kWaves);
+  }
 
   // Selection fragments: sel[par] picks channel 16*db + col out of the 32
   // channels of half db/2 (par = db % 2).
@@ -233,8 +380,21 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   float m_ref = -INFINITY, l_run = 0.f;  // m_ref in raw score units
   const float thr = kRescaleLog2 / sl2;
 
-  auto process = [&](const Tile<GQA, DR>& T) {
+  auto process = [&](Tile<GQA, DR>& T) {
     if (!T.ok) return;  // wave-uniform
+    if constexpr (STEP) {
+      // the appended row comes from the call's inputs, not from the cache
+      if (has_new && pos >= T.t0 && pos < T.t0 + kTile) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          if (min(16 * st + col, T.bound) == pos - T.t0) {
+            T.sa[st][0] = vnew[0];
+            T.sa[st][1] = vnew[1];
+            if constexpr (DR) T.kr[st] = knew;
+          }
+        }
+      }
+    }
     f32x4 s[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -348,6 +508,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   const int h = g * HPG + j;
   if (n_parts <= 1) {
     if (j < HPG) out[((int64_t)b * H + h) * kD + d] = (__bf16)(l > 0.f ? o / l : 0.f);
+    finish_step();
     return;
   }
   const int64_t slot0 = ((int64_t)b * H + h) * a.n_split;
@@ -359,43 +520,46 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     }
   }
   int32_t* counter = a.counters + (int64_t)b * G + g;
-  if (!arrive_last(counter, n_parts)) return;
-  if (j < HPG)
-    out[((int64_t)b * H + h) * kD + d] = (__bf16)merge_partials(a.ws_o, a.ws_ml, slot0, n_parts, d);
-  if (tid == 0) reset_counter(counter);
+  if (arrive_last(counter, n_parts)) {
+    if (j < HPG)
+      out[((int64_t)b * H + h) * kD + d] = (__bf16)merge_partials(a.ws_o, a.ws_ml, slot0, n_parts, d);
+    if (tid == 0) reset_counter(counter);
+  }
+  finish_step();
 }
 
-template <int HPG, bool DR, bool GQA>
+template <int HPG, bool DR, bool GQA, bool STEP>
 hipError_t mfma_paged(const DecodeLaunch& a, hipStream_t s) {
   const int pairs = a.B * a.n_split;
   const dim3 grid(((pairs + 7) / 8) * 8 * a.G);
   if (a.paged)
-    decode_mfma_kernel<HPG, true, DR, GQA><<<grid, 64 * kWaves, 0, s>>>(a);
+    decode_mfma_kernel<HPG, true, DR, GQA, STEP><<<grid, 64 * kWaves, 0, s>>>(a);
   else
-    decode_mfma_kernel<HPG, false, DR, GQA><<<grid, 64 * kWaves, 0, s>>>(a);
+    decode_mfma_kernel<HPG, false, DR, GQA, STEP><<<grid, 64 * kWaves, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <int HPG, bool GQA>
+template <int HPG, bool GQA, bool STEP>
 hipError_t mfma_dr(const DecodeLaunch& a, hipStream_t s) {
   if constexpr (!GQA) {
-    if (a.d_r > 0) return mfma_paged<HPG, true, false>(a, s);
+    if (a.d_r > 0) return mfma_paged<HPG, true, false, STEP>(a, s);
   }
-  return mfma_paged<HPG, false, GQA>(a, s);
+  return mfma_paged<HPG, false, GQA, STEP>(a, s);
 }
 
-template <bool GQA>
+template <bool GQA, bool STEP>
 hipError_t mfma_dispatch(const DecodeLaunch& a, hipStream_t s) {
   switch (a.H / a.G) {
-    case 1: return mfma_dr<1, GQA>(a, s);
-    case 2: return mfma_dr<2, GQA>(a, s);
-    default: return mfma_dr<4, GQA>(a, s);
+    case 1: return mfma_dr<1, GQA, STEP>(a, s);
+    case 2: return mfma_dr<2, GQA, STEP>(a, s);
+    default: return mfma_dr<4, GQA, STEP>(a, s);
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeLaunch& a, hipStream_t s) { return mfma_dispatch<false>(a, s); }
-hipError_t launch_gqa_mfma(const DecodeLaunch& a, hipStream_t s) { return mfma_dispatch<true>(a, s); }
+hipError_t launch_decode_mfma(const DecodeLaunch& a, hipStream_t s) { return mfma_dispatch<false, false>(a, s); }
+hipError_t launch_gqa_mfma(const DecodeLaunch& a, hipStream_t s) { return mfma_dispatch<true, false>(a, s); }
+hipError_t launch_step_mfma(const DecodeLaunch& a, hipStream_t s) { return mfma_dispatch<false, true>(a, s); }
 
 }  // namespace gva

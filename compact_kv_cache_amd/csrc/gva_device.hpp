@@ -35,11 +35,11 @@ template <> __device__ __forceinline__ __bf16 from_f64<__bf16>(double x) {
 
 // ---------------------------------------------------------------------------
 // RoPE on one channel pair (2i, 2i+1) at position pos: counter-clockwise turn
-// by pos * base^(-2i/d_r), in double precision.
+// by pos * theta_i (theta_i = base^(-2i/d_r), precomputed), in double
+// precision.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void rope_pair(double x0, double x1, double pos, int i, int d_r,
-                                          double base, double& y0, double& y1) {
-  const double theta = pow(base, -2.0 * (double)i / (double)d_r);
+__device__ __forceinline__ void rope_pair(double x0, double x1, double pos, double theta,
+                                          double& y0, double& y1) {
   double s, c;
   sincos(pos * theta, &s, &c);
   y0 = x0 * c - x1 * s;

@@ -5,7 +5,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 namespace gva {
+
+// RoPE frequencies theta_i = base^(-2i/d_r) for the d_r/2 channel pairs,
+// computed once on the host in double precision and passed by value.
+struct RopeTable {
+  double theta[16];
+};
+inline RopeTable make_rope_table(double base, int d_r) {
+  RopeTable t{};
+  for (int i = 0; i < d_r / 2 && i < 16; ++i) t.theta[i] = std::pow(base, -2.0 * i / d_r);
+  return t;
+}
 
 struct AppendLaunch {
   int B, G, d_r, n_new, capacity, num_blocks, max_blocks;
@@ -16,7 +29,7 @@ struct AppendLaunch {
   void* v_cache;
   void* kr_cache;
   const int32_t* block_table;
-  double rope_base;
+  RopeTable rope;
 };
 
 struct RopeQueryLaunch {
@@ -25,7 +38,7 @@ struct RopeQueryLaunch {
   const void* q_in;
   void* q_out;
   const int32_t* seq_lens;
-  double rope_base;
+  RopeTable rope;
 };
 
 // Decode problem, shared by the GVA kernels and the GQA comparison kernel.
@@ -34,7 +47,7 @@ struct DecodeLaunch {
   int split, n_split;  // split-K partition length and count
   bool paged, bf16;
   const void* q_nope;  // GQA: q
-  const void* q_rope;
+  const void* q_rope;  // rotated; fused step: before RoPE
   const void* M;
   const void* v_cache;
   const void* kr_cache;  // GQA: k_cache
@@ -42,19 +55,38 @@ struct DecodeLaunch {
   const int32_t* block_table;
   float scale;
   void* out;
-  // Workspace (split-K only): int32 arrival counters [B*G] (zero before the
-  // first call, left zero by every call), then float partials
-  // o [B*H*n_split*64] and (m, l) [B*H*n_split*2].
+  // Workspace: int32 arrival counters (zero before the first call, left zero
+  // by every call) -- [B*G] split-K, then [B] fused-step -- then float
+  // partials o [B*H*n_split*64] and (m, l) [B*H*n_split*2].
   int32_t* counters;
+  int32_t* counters_seq;
   float* ws_o;
   float* ws_ml;
+  // Fused step only (append one token + rotate the query + decode).
+  bool step;
+  int cap_tokens;          // token slots per sequence (capacity or pages * 64)
+  int32_t* seq_lens_rw;    // advanced by one, by the last workgroup of the sequence
+  void* v_cache_rw;        // receives the appended value rows
+  void* kr_cache_rw;       // receives the appended positional key
+  const void* v_new;       // [B][G][d_v]
+  const void* kr_new;      // [B][d_r] before RoPE
+  RopeTable rope;
 };
 
-// Workspace layout helpers (bytes).
-inline size_t ws_counter_bytes(int B, int G) { return (((size_t)B * G * 4) + 255) / 256 * 256; }
+// Workspace layout (bytes): counters, partials, rotated-query scratch.
+inline size_t ws_counter_bytes(int B, int G) {
+  return (((size_t)B * G + B) * 4 + 255) / 256 * 256;
+}
+inline size_t ws_partial_bytes(int B, int H, int n_split) {
+  return n_split <= 1 ? 0 : (size_t)B * H * n_split * (64 + 2) * sizeof(float);
+}
+inline size_t ws_qrot_bytes(int B, int H) { return (((size_t)B * H * 32 * 4) + 255) / 256 * 256; }
 inline size_t ws_total_bytes(int B, int H, int G, int n_split) {
   if (n_split <= 1) return 0;
-  return ws_counter_bytes(B, G) + (size_t)B * H * n_split * (64 + 2) * sizeof(float);
+  return ws_counter_bytes(B, G) + ws_partial_bytes(B, H, n_split);
+}
+inline size_t ws_step_bytes(int B, int H, int G, int n_split) {
+  return ws_counter_bytes(B, G) + ws_partial_bytes(B, H, n_split) + ws_qrot_bytes(B, H);
 }
 
 hipError_t launch_append(const AppendLaunch& a, hipStream_t s);
@@ -62,5 +94,6 @@ hipError_t launch_rope_query(const RopeQueryLaunch& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeLaunch& a, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeLaunch& a, hipStream_t s);  // bf16 only
 hipError_t launch_gqa_mfma(const DecodeLaunch& a, hipStream_t s);     // bf16 only
+hipError_t launch_step_mfma(const DecodeLaunch& a, hipStream_t s);    // bf16 only, a.step set
 
 }  // namespace gva

@@ -170,6 +170,37 @@ gva_status gva_decode(const gva_shape* shape, const void* q_nope, const void* q_
                       void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gva_decode_step - one whole decode step in a single call: append one token
+ * per sequence, rotate the query's positional slice, decode. Equivalent, bit
+ * for bit, to
+ *     gva_append(shape, v_new, kr_new, 1, seq_lens, v_cache, kr_cache, ...);
+ *     gva_rope_query(shape, q_rope, <rotated>, seq_lens, rope_base, ...);
+ *     gva_decode(shape, q_nope, <rotated>, M, v_cache, kr_cache, seq_lens, ...);
+ * (the decode loop of the [gqa] page: store the new token's state, then its
+ * query reads every cached token including itself). For bf16 this is one
+ * kernel launch; for fp32 the library runs the three kernels in sequence.
+ *   v_new    [B][G][d_v]     values of the new token
+ *   kr_new   [B][d_r]        its positional key BEFORE RoPE
+ *   q_nope   [B][H][d_n]     query content slice
+ *   q_rope   [B][H][d_r]     query positional slice BEFORE RoPE (not modified)
+ *   seq_lens int32 [B], in/out: the new token lands at seq_lens[b] and the
+ *            value grows by one (clamped to the capacity as in gva_append)
+ *   shape->max_seq_len must bound the lengths AFTER the append.
+ *   workspace at least gva_decode_step_workspace_bytes(shape) bytes, zero
+ *            before its first use, left reusable by every completed call.
+ * Other arguments as for gva_append / gva_decode.
+ */
+gva_status gva_decode_step(const gva_shape* shape, const void* v_new, const void* kr_new,
+                           const void* q_nope, const void* q_rope, const void* M, void* v_cache,
+                           void* kr_cache, int32_t* seq_lens, const int32_t* block_table, float scale,
+                           float rope_base, void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Bytes of device workspace gva_decode_step needs (never 0 for a valid
+ * shape). Returns 0 for an invalid shape. */
+size_t gva_decode_step_workspace_bytes(const gva_shape* shape);
+
+/*
  * gva_gqa_ref_decode - plain grouped-query attention decode over a K+V cache
  * of the same layout, the comparison point for bytes and time. GQA stores a
  * key and a value row per group and token ([gqa] sections on the K/V cache
