@@ -23,7 +23,11 @@ ARCH = os.environ.get("GVA_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU forms are kept out of the device code: hipcc would emit
 # them from ordinary float code otherwise.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The atomic optimizer is off: every atomic here is issued by one lane, and its
+# wave-aggregated rewrite reads the result back at once, which makes the wave
+# wait for all of its earlier loads (the tile stream) right after the atomic.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Wall",
           "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 

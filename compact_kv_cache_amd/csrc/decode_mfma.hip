@@ -166,6 +166,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   __shared__ float red_ml[kWaves][4][2];  // per-wave (max in log2 units, sum)
   __shared__ __bf16 qrot_sh[4][32];       // fused step: rotated query slices
   __shared__ __bf16 krot_sh[32];          // fused step: rotated appended key
+  __shared__ double theta_sh[16];         // fused step: RoPE angle steps
 
   const __bf16* vc = reinterpret_cast<const __bf16*>(a.v_cache);
   const __bf16* sc = reinterpret_cast<const __bf16*>(GQA ? a.kr_cache : a.v_cache);
@@ -198,25 +199,31 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   }
   // Fused step: waves 4..7 rotate the group's query slices (pairs
   // 0 .. HPG*d_r/2-1) and the appended key (the next d_r/2 pairs), exactly as
-  // gva_rope_query and gva_append do; the inputs are loaded here, the rotation
-  // runs after the barrier.
+  // gva_rope_query and gva_append do. Every lane loads one bf16 pair here
+  // (lanes with no pair re-read a valid one), unconditionally, so that no
+  // wave waits for it before the barrier; the rotation runs after the tile
+  // loads are in flight.
   const int half = d_r / 2;
   const int rot_i = (w - 4) * 64 + lane;  // pair handled by this lane (waves 4..7)
   const bool rot_q = STEP && DR && w >= 4 && rot_i < HPG * half;
   const bool rot_k = STEP && DR && w >= 4 && !rot_q && rot_i < HPG * half + half;
-  float rx0 = 0.f, rx1 = 0.f;
+  const int rot_j = rot_q ? rot_i / half : 0;  // head within the group
+  const int rot_p = rot_q ? rot_i % half : (rot_k ? rot_i - HPG * half : 0);  // pair index
+  uint32_t rx = 0;
   if constexpr (STEP && DR) {
-    if (rot_q) {
-      const int j = rot_i / half, i = rot_i % half;
-      const __bf16* qp = reinterpret_cast<const __bf16*>(a.q_rope) + ((int64_t)b * H + g * HPG + j) * d_r;
-      rx0 = (float)qp[2 * i];
-      rx1 = (float)qp[2 * i + 1];
-    } else if (rot_k) {
-      const int i = rot_i - HPG * half;
-      const __bf16* kn = reinterpret_cast<const __bf16*>(a.kr_new) + (int64_t)b * d_r;
-      rx0 = (float)kn[2 * i];
-      rx1 = (float)kn[2 * i + 1];
+    // copied with constant indices (scalar loads): a lane-indexed read of the
+    // kernel argument would be a vector load queued behind the tile loads
+    if (tid == 0) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) theta_sh[k] = a.rope.theta[k];
     }
+    // one pair from each source, selected afterwards (a per-lane choice of
+    // pointer would be compiled into a vector load of the kernel argument)
+    const __bf16* qsrc = reinterpret_cast<const __bf16*>(a.q_rope) + ((int64_t)b * H + g * HPG + rot_j) * d_r;
+    const __bf16* ksrc = reinterpret_cast<const __bf16*>(a.kr_new) + (int64_t)b * d_r;
+    const uint32_t rq = *reinterpret_cast<const uint32_t*>(qsrc + 2 * (rot_k ? 0 : rot_p));
+    const uint32_t rk = *reinterpret_cast<const uint32_t*>(ksrc + 2 * (rot_k ? rot_p : 0));
+    rx = rot_k ? rk : rq;
   }
   __syncthreads();
 
@@ -258,31 +265,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     }
   };
 
-  // Waves 4..7 have no query to prepare: they start the tile stream now,
-  // behind the prologue loads already queued (the barrier above orders them).
-  // Waves 0..3 start theirs once the queries are ready.
-  if constexpr (STEP && DR) {
-    if (rot_q) {
-      const int j = rot_i / half, i = rot_i % half;
-      double y0, y1;
-      rope_pair((double)rx0, (double)rx1, (double)max(n_full - 1, 0), a.rope.theta[i], y0, y1);
-      qrot_sh[j][2 * i] = from_f64<__bf16>(y0);
-      qrot_sh[j][2 * i + 1] = from_f64<__bf16>(y1);
-    } else if (rot_k) {
-      const int i = rot_i - HPG * half;
-      double y0, y1;
-      rope_pair((double)rx0, (double)rx1, (double)pos, a.rope.theta[i], y0, y1);
-      krot_sh[2 * i] = from_f64<__bf16>(y0);
-      krot_sh[2 * i + 1] = from_f64<__bf16>(y1);
-    }
-  }
-  Tile<GQA, DR> X, Y;
-  const bool early = w >= 4;
-  if (early) {
-    issue(X, w);
-    issue(Y, w + kWaves);
-  }
-
   // ---- queries into B-operand fragments ----------------------------------------
   if constexpr (!GQA) {
     if (w < HPG) {
@@ -303,8 +285,29 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   } else {
     if (w < HPG) qsh[w][lane] = (float)qn[((int64_t)b * H + g * HPG + w) * kD + lane];
   }
+  // ---- tile stream start --------------------------------------------------------
+  // Every wave issues its first two tiles here, at one program point: waves
+  // 0..HPG-1 after forming their absorbed query (so their prologue loads are
+  // not queued behind tiles they do not need yet), the other waves at once.
+  Tile<GQA, DR> X, Y;
+  issue(X, w);
+  issue(Y, w + kWaves);
+  // query slots past d_r contribute nothing (masked after the issue, so the
+  // wait for qr counts only the loads issued before it)
   if constexpr (DR && !STEP) {
-    if (8 * r >= d_r) qr.u = u32x4{0u, 0u, 0u, 0u};  // slots past d_r contribute nothing
+    if (8 * r >= d_r) qr.u = u32x4{0u, 0u, 0u, 0u};
+  }
+  if constexpr (STEP && DR) {
+    if (rot_q || rot_k) {
+      const double x0 = (double)__uint_as_float(rx << 16);
+      const double x1 = (double)__uint_as_float(rx & 0xffff0000u);
+      const double at = rot_q ? (double)max(n_full - 1, 0) : (double)pos;
+      double y0, y1;
+      rope_pair(x0, x1, at, theta_sh[rot_p], y0, y1);
+      __bf16* dst = rot_q ? &qrot_sh[rot_j][2 * rot_p] : &krot_sh[2 * rot_p];
+      dst[0] = from_f64<__bf16>(y0);
+      dst[1] = from_f64<__bf16>(y1);
+    }
   }
   __syncthreads();
   Frag qhi[2], qlo[2], knew;
@@ -340,9 +343,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
         krow = ((int64_t)b * a.capacity + pos) * d_r;
       }
       if (vrow >= 0) {
+        // lanes of column 0 hold channels 8r..8r+7 and 32+8r..32+8r+7 already
         __bf16* vdst = reinterpret_cast<__bf16*>(a.v_cache_rw) + vrow;
-        const __bf16* vn = reinterpret_cast<const __bf16*>(a.v_new) + ((int64_t)b * G + g) * kD;
-        if (lane < kD / 8) *reinterpret_cast<u32x4*>(vdst + 8 * lane) = ld16(vn, 8 * lane);
+        if (col == 0) {
+          *reinterpret_cast<u32x4*>(vdst + 8 * r) = vnew[0].u;
+          *reinterpret_cast<u32x4*>(vdst + 32 + 8 * r) = vnew[1].u;
+        }
         if constexpr (DR) {
           if (g == 0 && lane < d_r / 8) {
             Frag kk;
@@ -355,14 +361,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     }
   }
 
-  // Tiles of waves 0..3 are issued only now: issued earlier they would sit
-  // between the prologue's loads and their use (a wave stalls at load issue
-  // once the compute unit's request queues are full).
   if constexpr (STEP) take_ticket();
-  if (!early) {
-    issue(X, w);
-    issue(Y, w + kWaves);
-  }
 
   // Selection fragments: sel[par] picks channel 16*db + col out of the 32
   // channels of half db/2 (par = db % 2).

@@ -82,6 +82,29 @@ def test_auto_split_is_multiple_of_64():
         assert sp > 0 and sp % 64 == 0
 
 
+@pytest.mark.parametrize("B,n", [(16, 4096), (16, 4196), (16, 2100), (32, 8192), (4, 131072),
+                                 (64, 32868), (1, 256), (3, 1100)])
+def test_auto_split_partitions(B, n):
+    """Auto partitions: whole 64-token tiles, at least 8 per partition, and no
+    more (sequence, group, partition) workgroups than the 256 compute units
+    when the sequences are long enough to need more than one partition."""
+    s = _shape(B=B, split_tokens=0, max_seq_len=n, capacity=max(n, 64))
+    tiles_per = gva.gva_decode_split_tokens(s) // 64
+    tiles = -(-n // 64)
+    parts = -(-tiles // tiles_per)
+    assert tiles_per >= 8
+    if parts > 1:
+        assert parts * B * 4 <= 256
+    want = -(-256 // (B * 4))
+    assert tiles_per == max(8, -(-tiles // want))
+
+
+def test_auto_split_mid():
+    # 16 sequences of up to 4196 tokens (66 tiles): 4 partitions of 17 tiles
+    assert gva.gva_decode_split_tokens(_shape(B=16, split_tokens=0, max_seq_len=4196)) == 17 * 64
+    assert gva.gva_decode_split_tokens(_shape(B=16, split_tokens=0, max_seq_len=4096)) == 16 * 64
+
+
 def _decode_status(shape, ws=None, ws_bytes=0, **ptrs):
     p = dict(q_nope=FAKE, q_rope=FAKE, M=FAKE, v=FAKE, kr=FAKE, seq=FAKE, table=None, out=FAKE)
     p.update(ptrs)
