@@ -79,21 +79,40 @@ constexpr f32x4 kZero4 = {0.f, 0.f, 0.f, 0.f};
 constexpr int kWaves = 8;            // waves per workgroup
 constexpr float kRescaleLog2 = 8.f;  // move the reference max only beyond 2^8
 
-// Registers of one 64-token tile (4 sub-tiles of 16 tokens) for one wave.
+// One 64-token tile as loaded by one wave. Every 16-byte load instruction
+// covers 1 KB of contiguous cache memory: 8 whole 128-byte rows of the score
+// operand, or 1 KB of the positional-key rows (64 rows of 16*KR bytes).
 // GVA: sa = V rows, kr = positional keys. GQA: sa = K rows, vb = V rows.
-template <bool GQA, bool DR>
+template <bool GQA, int KR>
 struct Tile {
-  Frag sa[4][2];
-  Frag vb[GQA ? 4 : 1][2];
-  Frag kr[DR ? 4 : 1];
+  u32x4 sa[8];
+  u32x4 vb[GQA ? 8 : 1];
+  u32x4 kr[KR > 0 ? KR : 1];
   int t0;     // first token of the tile
   int bound;  // last row of the tile that was read (rows past it re-read it)
   bool ok;    // tile exists and its page is valid (wave-uniform)
   bool full;  // all 64 tokens are inside the partition (wave-uniform)
 };
 
-template <int HPG, bool PAGED, bool DR, bool GQA, bool STEP>
+// The same tile as matrix-core operands (4 sub-tiles of 16 tokens), read back
+// from the wave's LDS stage: lane (col, r) holds row 16*st + col, channels
+// 32*h + 8*r .. +7 in sa[st][h].
+template <bool GQA, bool DR>
+struct Frags {
+  Frag sa[4][2];
+  Frag vb[GQA ? 4 : 1][2];
+  Frag kr[DR ? 4 : 1];
+  int t0, bound;
+  bool ok, full;
+};
+
+// 16-byte chunk permutation inside a 128-byte staged row. Reading one chunk
+// position of 16 consecutive rows then touches 16 distinct bank groups.
+__device__ __forceinline__ int stage_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+template <int HPG, bool PAGED, int KR, bool GQA, bool STEP>
 __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunch a) {
+  constexpr bool DR = KR > 0;  // positional slice present (d_r = 8 * KR)
   static_assert(!(GQA && DR), "GQA reference has no positional slice");
   static_assert(!(GQA && STEP), "the fused step is GVA only");
   constexpr bool QLO = !GQA;  // GQA queries are exact in bf16
@@ -172,7 +191,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   const __bf16* sc = reinterpret_cast<const __bf16*>(GQA ? a.kr_cache : a.v_cache);
   const __bf16* kc = reinterpret_cast<const __bf16*>(a.kr_cache);
   const __bf16* qn = reinterpret_cast<const __bf16*>(a.q_nope);
-  const int kr_off = DR ? 8 * min(r, d_r / 8 - 1) : 0;  // lanes past d_r re-read a valid slice
+  const int kr_off = DR ? 8 * min(r, KR - 1) : 0;  // lanes past d_r re-read a valid slice
 
   // ---- prologue loads ------------------------------------------------------------
   Frag mA[4][2], qB[2];
@@ -228,7 +247,13 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   __syncthreads();
 
   // ---- tile loads ---------------------------------------------------------------
-  auto issue = [&](Tile<GQA, DR>& T, int k) {
+  // Stage of this wave in LDS: score-operand rows (swizzled 16-byte chunks),
+  // then the GQA value rows or the positional keys (row-major).
+  constexpr int kStageBytes = 8192 + (GQA ? 8192 : 1024 * KR);
+  __shared__ __attribute__((aligned(16))) char stage_lds[kWaves * kStageBytes];
+  char* const stage_w = stage_lds + w * kStageBytes;
+
+  auto issue = [&](Tile<GQA, KR>& T, int k) {
     const int t0 = t_begin + k * kTile;
     bool ok = k < n_tiles;
     int64_t vbase = 0, kbase = 0;
@@ -250,18 +275,57 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     // tile reads row 0 of the cache
     const int bound = ok ? min(kTile - 1, t_end - 1 - t0) : 0;
     T.bound = bound;
-    const __bf16* vp = sc + vbase;
+    // instruction i, lane l fills staged row 8i + l/8, chunk position l%8,
+    // with chunk (l%8) ^ swizzle(row) of cache row min(row, bound)
+    const char* sp = reinterpret_cast<const char*>(sc + vbase);
+    const char* vp = reinterpret_cast<const char*>(vc + vbase);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * i + (lane >> 3);
+      const int off = min(row, bound) * (kD * 2) + 16 * ((lane & 7) ^ stage_swizzle(row));
+      T.sa[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sp + off));
+      if constexpr (GQA) T.vb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + off));
+    }
+    if constexpr (DR) {
+      const char* kp = reinterpret_cast<const char*>(kc + kbase);
+#pragma unroll
+      for (int i = 0; i < KR; ++i) {
+        const int byte = 1024 * i + 16 * lane;
+        const int row = byte / (16 * KR), in_row = byte % (16 * KR);
+        T.kr[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(kp + min(row, bound) * (16 * KR) + in_row));
+      }
+    }
+  };
+  // Registers -> LDS stage (plain contiguous stores), then the operand
+  // fragments back. LDS operations of one wave complete in order, so the
+  // fragments see the stage and the next stage cannot overtake them.
+  auto stage = [&](const Tile<GQA, KR>& T) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<u32x4*>(stage_w + 1024 * i + 16 * lane) = T.sa[i];
+      if constexpr (GQA) *reinterpret_cast<u32x4*>(stage_w + 8192 + 1024 * i + 16 * lane) = T.vb[i];
+    }
+    if constexpr (DR) {
+#pragma unroll
+      for (int i = 0; i < KR; ++i) *reinterpret_cast<u32x4*>(stage_w + 8192 + 1024 * i + 16 * lane) = T.kr[i];
+    }
+  };
+  auto fragments = [&](Frags<GQA, DR>& F, const Tile<GQA, KR>& T) {
+    F.t0 = T.t0;
+    F.bound = T.bound;
+    F.ok = T.ok;
+    F.full = T.full;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const int row = min(16 * st + col, bound);
-      const int off = row * kD + 8 * r;
-      T.sa[st][0].u = ld16_stream(vp, off);
-      T.sa[st][1].u = ld16_stream(vp, off + 32);
-      if constexpr (GQA) {
-        T.vb[st][0].u = ld16_stream(vc + vbase, off);
-        T.vb[st][1].u = ld16_stream(vc + vbase, off + 32);
+      const int row = 16 * st + col;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int at = row * (kD * 2) + 16 * ((4 * h + r) ^ stage_swizzle(row));
+        F.sa[st][h].u = *reinterpret_cast<const u32x4*>(stage_w + at);
+        if constexpr (GQA) F.vb[st][h].u = *reinterpret_cast<const u32x4*>(stage_w + 8192 + at);
       }
-      if constexpr (DR) T.kr[st].u = ld16_stream(kc + kbase, row * d_r + kr_off);
+      if constexpr (DR) F.kr[st].u = *reinterpret_cast<const u32x4*>(stage_w + 8192 + row * (16 * KR) + 2 * kr_off);
     }
   };
 
@@ -289,7 +353,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   // Every wave issues its first two tiles here, at one program point: waves
   // 0..HPG-1 after forming their absorbed query (so their prologue loads are
   // not queued behind tiles they do not need yet), the other waves at once.
-  Tile<GQA, DR> X, Y;
+  Tile<GQA, KR> X, Y;
   issue(X, w);
   issue(Y, w + kWaves);
   // query slots past d_r contribute nothing (masked after the issue, so the
@@ -379,7 +443,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   float m_ref = -INFINITY, l_run = 0.f;  // m_ref in raw score units
   const float thr = kRescaleLog2 / sl2;
 
-  auto process = [&](Tile<GQA, DR>& T) {
+  auto process = [&](Frags<GQA, DR>& T) {
     if (!T.ok) return;  // wave-uniform
     if constexpr (STEP) {
       // the appended row comes from the call's inputs, not from the cache
@@ -467,12 +531,19 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     }
   };
 
+  // Each tile is staged, its registers are reloaded at once with the tile
+  // two rounds ahead, and the math runs on the staged copy.
+  Frags<GQA, DR> F;
   for (int k = w; k < n_tiles; k += 2 * kWaves) {
-    process(X);
+    stage(X);
+    fragments(F, X);
     issue(X, k + 2 * kWaves);
+    process(F);
     if (k + kWaves >= n_tiles) break;
-    process(Y);
+    stage(Y);
+    fragments(F, Y);
     issue(Y, k + 3 * kWaves);
+    process(F);
   }
 
   // ---- merge the waves ----------------------------------------------------------------
@@ -527,23 +598,30 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   finish_step();
 }
 
-template <int HPG, bool DR, bool GQA, bool STEP>
+template <int HPG, int KR, bool GQA, bool STEP>
 hipError_t mfma_paged(const DecodeLaunch& a, hipStream_t s) {
   const int pairs = a.B * a.n_split;
   const dim3 grid(((pairs + 7) / 8) * 8 * a.G);
   if (a.paged)
-    decode_mfma_kernel<HPG, true, DR, GQA, STEP><<<grid, 64 * kWaves, 0, s>>>(a);
+    decode_mfma_kernel<HPG, true, KR, GQA, STEP><<<grid, 64 * kWaves, 0, s>>>(a);
   else
-    decode_mfma_kernel<HPG, false, DR, GQA, STEP><<<grid, 64 * kWaves, 0, s>>>(a);
+    decode_mfma_kernel<HPG, false, KR, GQA, STEP><<<grid, 64 * kWaves, 0, s>>>(a);
   return hipGetLastError();
 }
 
+// d_r = 8 * KR (validated on the host: 0, 8, 16, 24 or 32)
 template <int HPG, bool GQA, bool STEP>
 hipError_t mfma_dr(const DecodeLaunch& a, hipStream_t s) {
   if constexpr (!GQA) {
-    if (a.d_r > 0) return mfma_paged<HPG, true, false, STEP>(a, s);
+    switch (a.d_r / 8) {
+      case 1: return mfma_paged<HPG, 1, false, STEP>(a, s);
+      case 2: return mfma_paged<HPG, 2, false, STEP>(a, s);
+      case 3: return mfma_paged<HPG, 3, false, STEP>(a, s);
+      case 4: return mfma_paged<HPG, 4, false, STEP>(a, s);
+      default: break;
+    }
   }
-  return mfma_paged<HPG, false, GQA, STEP>(a, s);
+  return mfma_paged<HPG, 0, GQA, STEP>(a, s);
 }
 
 template <bool GQA, bool STEP>
