@@ -13,8 +13,15 @@ cache; the default workload is B=16, S=4096, H=16, G=4, d_v=d_n=64, d_r=16,
 bf16 (the mid workload), on seeded synthetic data.
 
 Prints one JSON line. `value` = steps/s of the whole path (graph-replayed, so
-host launch overhead is excluded); the decode kernel's roofline is measured
-with HIP events around each gva_decode call on the stream it runs on.
+host launch overhead is excluded). `roofline` describes the one kernel of the
+timed region (the fused step): algorithmic cache bytes per step over its
+average launch duration, from HIP events around the graph replay on the
+stream the kernels run on. gva_decode alone (one kernel, no append) is timed
+the same way and reported beside it.
+
+`--mode gqa` instead times gva_decode against the same-shape GQA reference
+(gva_gqa_ref_decode, K and V caches) on the wide workload and reports the
+time ratio beside the ratio of the bytes each must read.
 """
 from __future__ import annotations
 
@@ -46,6 +53,9 @@ def parse():
                    help="split-K partition length in tokens (-1 = the workload's, 0 = automatic)")
     p.add_argument("--profile-decode", type=int, default=0,
                    help="only run N eager decodes (for rocprofv3 runs) and exit")
+    p.add_argument("--profile-step", type=int, default=0,
+                   help="only run N eager fused steps (for rocprofv3 runs) and exit")
+    p.add_argument("--mode", choices=["step", "gqa"], default="step")
     return p.parse_args()
 
 
@@ -69,6 +79,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.mode == "gqa":
+        gqa_compare(args)
+        return
     wl = W.WORKLOADS[args.workload]
     if args.split >= 0:
         wl = wl.replace(split_tokens=args.split)
@@ -153,6 +166,12 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"profile_decode": args.profile_decode, "replicas": R}))
         return
+    if args.profile_step:
+        for i in range(args.profile_step):
+            fused_step(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_step": args.profile_step, "replicas": R}))
+        return
 
     i_step = 0
     for k in range(Wm):  # warm both forms of the step
@@ -236,7 +255,9 @@ def main():
         torch.cuda.synchronize()
         ms_dec_graph = e0.elapsed_time(e1) / K
     ms_launch = ms_dec_graph if ms_dec_graph is not None else dec_ms_mean
-    achieved = dec_bytes_mean / (ms_launch * 1e-3) / 1e9
+    dec_gbps = dec_bytes_mean / (ms_launch * 1e-3) / 1e9
+    # the timed region launches one kernel per step (the fused step)
+    achieved = mean_step_bytes / (ms_step * 1e-3) / 1e9
 
     traffic = None  # filled from profiles only while the kernel source matches (see design doc)
 
@@ -260,19 +281,95 @@ def main():
                    "replicas": R, "split_tokens": gva.gva_decode_split_tokens(shape_at(0, wl.S)),
                    "graph": use_graph, "step": "gva_decode_step (one launch)"},
         "cache_read_GBps": round(mean_step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_kernel_us": round(ms_step * 1e3, 3),
         "decode_us": round(ms_launch * 1e3, 3),
+        "decode_cache_read_GBps": round(dec_gbps, 1),
+        "decode_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
         "decode_event_per_call_us": round(dec_ms_mean * 1e3, 3),
         "eager_ms_per_step": round(ms_eager, 6),
         "three_call_steps_per_s": None if ms_three is None else round(1e3 / ms_three, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic,
-                     "bytes_per_launch": dec_bytes_mean},
+                     "traffic": traffic, "kernel": "fused decode step",
+                     "bytes_per_launch": mean_step_bytes},
     }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def gqa_compare(args):
+    """gva_decode and gva_gqa_ref_decode on the same B, S, G, H and d_v = d_h:
+    the GVA cache (G value rows + one positional key per token) against the
+    GQA cache (G key rows + G value rows per token). Each is timed as K
+    back-to-back launches in one graph over cold replicas."""
+    import numpy as np
+    import torch
+
+    import compact_kv_cache_amd as gva
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS["wide_dr24" if args.workload == "mid_bf16" else args.workload]
+    K = args.steps
+    out = {}
+    for kind in ("gva", "gqa"):
+        d_r = wl.d_r if kind == "gva" else 0
+        bpt = gva.gva_cache_bytes_per_token(wl.G, wl.d_v, d_r, wl.dtype) * (1 if kind == "gva" else 2)
+        nbytes = wl.B * wl.S * bpt
+        R = max(2, math.ceil(512e6 / nbytes))
+        rng = np.random.Generator(np.random.PCG64(wl.seed + (1 if kind == "gva" else 2)))
+        # cache contents do not change the timing; seeded N(0,1) values, bf16
+        base_v = torch.from_numpy(rng.standard_normal((wl.B, wl.G, wl.S, wl.d_v), dtype=np.float32)).to(dev).bfloat16()
+        if kind == "gva":
+            second = torch.from_numpy(rng.standard_normal((wl.B, wl.S, d_r), dtype=np.float32)).to(dev).bfloat16()
+        else:
+            second = torch.from_numpy(rng.standard_normal((wl.B, wl.G, wl.S, wl.d_v), dtype=np.float32)).to(dev).bfloat16()
+        reps = [(base_v.clone(), second.clone()) for _ in range(R)]
+        del base_v, second
+        seq = torch.full((wl.B,), wl.S, dtype=torch.int32, device=dev)
+        shape = gva.make_shape(wl.B, wl.H, wl.G, wl.d_n, wl.d_v, d_r, capacity=wl.S, max_seq_len=wl.S,
+                               split_tokens=wl.split_tokens, dtype=wl.dtype)
+        ws = torch.zeros(max(gva.gva_decode_workspace_bytes(shape), 4) // 4 + 1, dtype=torch.float32, device=dev)
+        o = torch.empty(wl.B, wl.H, wl.d_v, dtype=torch.bfloat16, device=dev)
+        q = torch.randn(wl.B, wl.H, wl.d_n, device=dev).bfloat16()
+        qr = torch.randn(wl.B, wl.H, max(d_r, 1), device=dev).bfloat16()[:, :, :d_r].contiguous()
+        M = (torch.randn(wl.H, wl.d_v, wl.d_n, device=dev) / 8).bfloat16()
+
+        def call(i):
+            a, b2 = reps[i % R]
+            if kind == "gva":
+                gva.gva_decode(shape, q, qr, M, a, b2, seq, None, wl.scale, o, ws)
+            else:
+                gva.gva_gqa_ref_decode(shape, q, b2, a, seq, None, 0.125, o, ws)
+
+        for i in range(2 * R):
+            call(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                call(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / K * 1e3
+        out[kind] = {"us": round(us, 3), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+                     "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4), "replicas": R}
+        del reps
+        torch.cuda.empty_cache()
+    res = {"mode": "gqa_compare",
+           "config": {"workload": f"{wl.name}: B={wl.B} S={wl.S} H={wl.H} G={wl.G} d_v={wl.d_v} "
+                                  f"d_r={wl.d_r} {wl.dtype}, contiguous caches, cold replicas",
+                      "steps": K},
+           "gva": out["gva"], "gqa": out["gqa"],
+           "time_ratio_gqa_over_gva": round(out["gqa"]["us"] / out["gva"]["us"], 3),
+           "byte_ratio_gqa_over_gva": round(out["gqa"]["bytes"] / out["gva"]["bytes"], 3)}
+    print(json.dumps(res), flush=True)
 
 
 def cpu_baseline(wl, seconds: float):

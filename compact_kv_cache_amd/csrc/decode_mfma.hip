@@ -22,7 +22,7 @@
 //   scores     S^T[tok][col] = V[tok][:] . q'[head(col)][:] + k_r[tok] . q_rope:
 //              A = V rows exactly as loaded (lane l: token l%16, 8 channels),
 //              B = queries with the group's heads repeated across the 16
-//              columns; q' is split into bf16 hi + lo parts.
+//              columns; q' is accumulated in fp32 and rounded to bf16 once.
 //   transpose  C[tok][c] = V[tok][:] . E[:][c], E a 0/1 selection of 16
 //              channels: V^T in the A layout of the next product, exactly.
 //   P.V        O^T[ch][col] += V^T[ch][tok] . P^T[tok][col] over 32 tokens; B =
@@ -91,16 +91,15 @@ struct Tile {
   int t0;     // first token of the tile
   int bound;  // last row of the tile that was read (rows past it re-read it)
   bool ok;    // tile exists and its page is valid (wave-uniform)
-  bool full;  // all 64 tokens are inside the partition (wave-uniform)
 };
 
 // The same tile as matrix-core operands (4 sub-tiles of 16 tokens), read back
 // from the wave's LDS stage: lane (col, r) holds row 16*st + col, channels
-// 32*h + 8*r .. +7 in sa[st][h].
-template <bool GQA, bool DR>
+// 32*h + 8*r .. +7 in sa[st][h]. (The GQA value rows are read from the stage
+// where they are used, which keeps the kernel within its registers.)
+template <bool DR>
 struct Frags {
   Frag sa[4][2];
-  Frag vb[GQA ? 4 : 1][2];
   Frag kr[DR ? 4 : 1];
   int t0, bound;
   bool ok, full;
@@ -115,7 +114,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   constexpr bool DR = KR > 0;  // positional slice present (d_r = 8 * KR)
   static_assert(!(GQA && DR), "GQA reference has no positional slice");
   static_assert(!(GQA && STEP), "the fused step is GVA only");
-  constexpr bool QLO = !GQA;  // GQA queries are exact in bf16
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
   const int col = lane & 15, r = lane >> 4;                 // MFMA column / lane group
@@ -130,62 +128,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   if (p >= pairs) return;
   const int b = p / a.n_split, split = p % a.n_split;
 
-  // Sequence length. Fused step: the token appended by this call sits at
-  // position `pos` (the stored length) unless the cache is full.
-  const int stored = max(a.seq_lens[b], 0);
-  int pos = 0, n_full = stored;
-  bool has_new = false;
-  if constexpr (STEP) {
-    pos = stored;
-    has_new = pos < a.cap_tokens;
-    n_full = has_new ? pos + 1 : a.cap_tokens;
-  }
-  const int n = min(n_full, a.max_seq_len);
-  const int n_parts = (n + a.split - 1) / a.split;
-
-  // Fused step: a workgroup takes its ticket only after a barrier that
-  // follows every wave's read of seq_lens[b] (the barrier waits for the scalar
-  // read to return). The last of the sequence's G * n_split tickets stores the
-  // new length, which therefore cannot be observed by any workgroup of this
-  // call. Participating workgroups take the ticket just before their tile
-  // stream, so its round trip hides under the tile loads.
-  int ticket = 0;
-  auto take_ticket = [&]() {
-    if (tid == 0)
-      ticket = __hip_atomic_fetch_add(a.counters_seq + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  auto finish_step = [&]() {
-    if constexpr (STEP) {
-      if (tid == 0 && ticket == G * a.n_split - 1) {
-        a.seq_lens_rw[b] = n_full;
-        __hip_atomic_store(a.counters_seq + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  };
-  if (split >= max(n_parts, 1)) {  // uniform per workgroup
-    if constexpr (STEP) {
-      __syncthreads();
-      take_ticket();
-      finish_step();
-    }
-    return;
-  }
+  // Partition range from the host-side bound max_seq_len. It does not depend
+  // on the stored lengths, so the first tiles are requested before seq_lens[b]
+  // has arrived; rows past the stored length are cleared before any use.
   const int t_begin = split * a.split;
-  const int t_end = min(n, t_begin + a.split);
-  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;  // 0 only when n == 0
+  const int t_end_max = min(a.max_seq_len, t_begin + a.split);
+  const int tiles_max = max(t_end_max - t_begin + kTile - 1, 0) / kTile;
   const float sl2 = a.scale * kLog2e;
   const int jcol = col % HPG;        // head (within the group) of this lane's column
   const int h_col = g * HPG + jcol;  // its global head index
-  // Query preparation: wave w < HPG forms head w of the group; waves 4..7
-  // rotate the fused step's positional slices meanwhile.
-  const int h_w = g * HPG + min(w, HPG - 1);
 
   __shared__ float qsh[4][kD];            // [head][channel] absorbed queries
   __shared__ float red_o[kWaves][4][kD];  // per-wave unnormalized outputs
   __shared__ float red_ml[kWaves][4][2];  // per-wave (max in log2 units, sum)
   __shared__ __bf16 qrot_sh[4][32];       // fused step: rotated query slices
-  __shared__ __bf16 krot_sh[32];          // fused step: rotated appended key
-  __shared__ double theta_sh[16];         // fused step: RoPE angle steps
+  __shared__ __attribute__((aligned(16))) __bf16 krot_sh[32];  // fused step: rotated appended key
+  __shared__ __attribute__((aligned(16))) __bf16 vnew_sh[kD];  // fused step: appended value row
 
   const __bf16* vc = reinterpret_cast<const __bf16*>(a.v_cache);
   const __bf16* sc = reinterpret_cast<const __bf16*>(GQA ? a.kr_cache : a.v_cache);
@@ -193,35 +151,41 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   const __bf16* qn = reinterpret_cast<const __bf16*>(a.q_nope);
   const int kr_off = DR ? 8 * min(r, KR - 1) : 0;  // lanes past d_r re-read a valid slice
 
-  // ---- prologue loads ------------------------------------------------------------
-  Frag mA[4][2], qB[2];
+  // ---- prologue loads (independent of the stored lengths) ------------------------
+  // Query preparation is split evenly: wave w forms half w / 4 (32 channels) of
+  // head (w % 4) % HPG of the group (with fewer heads, waves repeat a half and
+  // store the same values).
+  const int gm_j = (w & 3) % HPG, gm_half = w >> 2;
+  const int h_w = g * HPG + gm_j;
+  Frag mA[2][2], qB[2];
+  float qv = 0.f;
   if constexpr (!GQA) {
-    if (w < HPG) {
+    const __bf16* Mh = reinterpret_cast<const __bf16*>(a.M) + (int64_t)h_w * kD * kD;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int chan = 32 * (mb >> 1) + 8 * (col >> 2) + 4 * (mb & 1) + (col & 3);
-        const __bf16* Mh = reinterpret_cast<const __bf16*>(a.M) + (int64_t)h_w * kD * kD;
+    for (int m = 0; m < 2; ++m) {
+      const int mb = 2 * gm_half + m;
+      const int chan = 32 * (mb >> 1) + 8 * (col >> 2) + 4 * (mb & 1) + (col & 3);
 #pragma unroll
-        for (int kc2 = 0; kc2 < 2; ++kc2) mA[mb][kc2].u = ld16(Mh, chan * kD + 32 * kc2 + 8 * r);
-      }
-#pragma unroll
-      for (int kc2 = 0; kc2 < 2; ++kc2) qB[kc2].u = ld16(qn + ((int64_t)b * H + h_w) * kD, 32 * kc2 + 8 * r);
+      for (int kc2 = 0; kc2 < 2; ++kc2) mA[m][kc2].u = ld16(Mh, chan * kD + 32 * kc2 + 8 * r);
     }
+#pragma unroll
+    for (int kc2 = 0; kc2 < 2; ++kc2) qB[kc2].u = ld16(qn + ((int64_t)b * H + h_w) * kD, 32 * kc2 + 8 * r);
+  } else {
+    qv = (float)qn[((int64_t)b * H + h_w) * kD + lane];
   }
-  Frag qr, vnew[2];
+  Frag qr;
   if constexpr (DR && !STEP)
     qr.u = ld16(reinterpret_cast<const __bf16*>(a.q_rope) + ((int64_t)b * H + h_col) * d_r, kr_off);
-  if constexpr (STEP) {
-    const __bf16* vn = reinterpret_cast<const __bf16*>(a.v_new) + ((int64_t)b * G + g) * kD;
-    vnew[0].u = ld16(vn, 8 * r);
-    vnew[1].u = ld16(vn, 32 + 8 * r);
-  }
+  // Fused step: the appended value row (lane l holds channels 8*(l%8) .. +7);
+  // it is kept in LDS, not in registers, for the one tile that holds it.
+  u32x4 vnew_l = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (STEP) vnew_l = ld16(reinterpret_cast<const __bf16*>(a.v_new) + ((int64_t)b * G + g) * kD, 8 * (lane & 7));
   // Fused step: waves 4..7 rotate the group's query slices (pairs
   // 0 .. HPG*d_r/2-1) and the appended key (the next d_r/2 pairs), exactly as
-  // gva_rope_query and gva_append do. Every lane loads one bf16 pair here
-  // (lanes with no pair re-read a valid one), unconditionally, so that no
-  // wave waits for it before the barrier; the rotation runs after the tile
-  // loads are in flight.
+  // gva_rope_query and gva_append do. Every lane loads one bf16 pair of each
+  // source (lanes with no pair re-read a valid one) and selects afterwards: a
+  // per-lane choice of pointer would be compiled into a vector load of the
+  // kernel argument, queued behind the tile loads.
   const int half = d_r / 2;
   const int rot_i = (w - 4) * 64 + lane;  // pair handled by this lane (waves 4..7)
   const bool rot_q = STEP && DR && w >= 4 && rot_i < HPG * half;
@@ -230,21 +194,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   const int rot_p = rot_q ? rot_i % half : (rot_k ? rot_i - HPG * half : 0);  // pair index
   uint32_t rx = 0;
   if constexpr (STEP && DR) {
-    // copied with constant indices (scalar loads): a lane-indexed read of the
-    // kernel argument would be a vector load queued behind the tile loads
-    if (tid == 0) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) theta_sh[k] = a.rope.theta[k];
-    }
-    // one pair from each source, selected afterwards (a per-lane choice of
-    // pointer would be compiled into a vector load of the kernel argument)
     const __bf16* qsrc = reinterpret_cast<const __bf16*>(a.q_rope) + ((int64_t)b * H + g * HPG + rot_j) * d_r;
     const __bf16* ksrc = reinterpret_cast<const __bf16*>(a.kr_new) + (int64_t)b * d_r;
     const uint32_t rq = *reinterpret_cast<const uint32_t*>(qsrc + 2 * (rot_k ? 0 : rot_p));
     const uint32_t rk = *reinterpret_cast<const uint32_t*>(ksrc + 2 * (rot_k ? rot_p : 0));
     rx = rot_k ? rk : rq;
   }
-  __syncthreads();
 
   // ---- tile loads ---------------------------------------------------------------
   // Stage of this wave in LDS: score-operand rows (swizzled 16-byte chunks),
@@ -253,9 +208,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   __shared__ __attribute__((aligned(16))) char stage_lds[kWaves * kStageBytes];
   char* const stage_w = stage_lds + w * kStageBytes;
 
-  auto issue = [&](Tile<GQA, KR>& T, int k) {
+  // Tile k of this partition, rows clamped to [t_begin, t_hi) (t_hi is the
+  // partition end from max_seq_len for the first round, the stored end after).
+  auto issue = [&](Tile<GQA, KR>& T, int k, int t_hi, int tiles) {
     const int t0 = t_begin + k * kTile;
-    bool ok = k < n_tiles;
+    bool ok = k < tiles;
     int64_t vbase = 0, kbase = 0;
     if constexpr (PAGED) {
       const int jb = min(t0 / kBlock, a.max_blocks - 1);
@@ -270,10 +227,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     if (!ok) vbase = kbase = 0;
     T.t0 = t0;
     T.ok = ok;
-    T.full = ok && t0 + kTile <= t_end;
     // last row this tile may touch: rows past the end re-read it; a missing
     // tile reads row 0 of the cache
-    const int bound = ok ? min(kTile - 1, t_end - 1 - t0) : 0;
+    const int bound = ok ? min(kTile - 1, t_hi - 1 - t0) : 0;
     T.bound = bound;
     // instruction i, lane l fills staged row 8i + l/8, chunk position l%8,
     // with chunk (l%8) ^ swizzle(row) of cache row min(row, bound)
@@ -297,6 +253,57 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       }
     }
   };
+  Tile<GQA, KR> X;
+  // The prologue loads stay ahead of the tile loads (a load's result is only
+  // counted complete once every earlier load of the wave is).
+  __builtin_amdgcn_sched_barrier(0);
+  issue(X, w, t_end_max, tiles_max);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- stored length --------------------------------------------------------------
+  // Fused step: the token appended by this call sits at position `pos` (the
+  // stored length) unless the cache is full.
+  const int stored = max(a.seq_lens[b], 0);
+  int pos = 0, n_full = stored;
+  bool has_new = false;
+  if constexpr (STEP) {
+    pos = stored;
+    has_new = pos < a.cap_tokens;
+    n_full = has_new ? pos + 1 : a.cap_tokens;
+  }
+  const int n = min(n_full, a.max_seq_len);
+  const int n_parts = (n + a.split - 1) / a.split;
+
+  // Fused step: a workgroup takes its ticket only after a barrier that
+  // follows every wave's read of seq_lens[b] (the barrier waits for the scalar
+  // read to return). The last of the sequence's G * n_split tickets stores the
+  // new length, which therefore cannot be observed by any workgroup of this
+  // call. Participating workgroups take the ticket once their tile stream is
+  // under way, so its round trip hides under the tile loads.
+  int ticket = 0;
+  auto take_ticket = [&]() {
+    if (tid == 0)
+      ticket = __hip_atomic_fetch_add(a.counters_seq + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto finish_step = [&]() {
+    if constexpr (STEP) {
+      if (tid == 0 && ticket == G * a.n_split - 1) {
+        a.seq_lens_rw[b] = n_full;
+        __hip_atomic_store(a.counters_seq + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  };
+  if (split >= max(n_parts, 1)) {  // uniform per workgroup; its tile loads are simply dropped
+    if constexpr (STEP) {
+      __syncthreads();
+      take_ticket();
+      finish_step();
+    }
+    return;
+  }
+  const int t_end = min(n, t_begin + a.split);
+  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;  // 0 only when n == 0
+
   // Registers -> LDS stage (plain contiguous stores), then the operand
   // fragments back. LDS operations of one wave complete in order, so the
   // fragments see the stage and the next stage cannot overtake them.
@@ -311,11 +318,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       for (int i = 0; i < KR; ++i) *reinterpret_cast<u32x4*>(stage_w + 8192 + 1024 * i + 16 * lane) = T.kr[i];
     }
   };
-  auto fragments = [&](Frags<GQA, DR>& F, const Tile<GQA, KR>& T) {
+  auto fragments = [&](Frags<DR>& F, const Tile<GQA, KR>& T) {
     F.t0 = T.t0;
     F.bound = T.bound;
     F.ok = T.ok;
-    F.full = T.full;
+    F.full = T.ok && T.t0 + kTile <= t_end;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int row = 16 * st + col;
@@ -323,43 +330,59 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       for (int h = 0; h < 2; ++h) {
         const int at = row * (kD * 2) + 16 * ((4 * h + r) ^ stage_swizzle(row));
         F.sa[st][h].u = *reinterpret_cast<const u32x4*>(stage_w + at);
-        if constexpr (GQA) F.vb[st][h].u = *reinterpret_cast<const u32x4*>(stage_w + 8192 + at);
       }
       if constexpr (DR) F.kr[st].u = *reinterpret_cast<const u32x4*>(stage_w + 8192 + row * (16 * KR) + 2 * kr_off);
     }
-  };
-
-  // ---- queries into B-operand fragments ----------------------------------------
-  if constexpr (!GQA) {
-    if (w < HPG) {
-      f32x4 D[4];
+    // Rows at or past the stored end (a first-round tile may hold stale or
+    // unwritten cache rows there) become zeros: their scores are masked, and
+    // zero rows keep the probability-weighted sum exact.
+    if (!F.full) {
+      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        D[mb] = mma(mA[mb][0], qB[0], kZero4);
-        D[mb] = mma(mA[mb][1], qB[1], D[mb]);
-      }
-      // lane (col 0, group r) holds q'[32kc + 8r + e] in D[2kc + e / 4][e % 4]
-      if (col == 0) {
+      for (int st = 0; st < 4; ++st) {
+        const bool past = T.t0 + 16 * st + col >= t_end;
 #pragma unroll
-        for (int kc2 = 0; kc2 < 2; ++kc2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qsh[w][32 * kc2 + 8 * r + e] = D[2 * kc2 + (e >> 2)][e & 3];
+        for (int h = 0; h < 2; ++h) {
+          F.sa[st][h].u = past ? z : F.sa[st][h].u;
+        }
+        if constexpr (DR) F.kr[st].u = past ? z : F.kr[st].u;
       }
     }
-  } else {
-    if (w < HPG) qsh[w][lane] = (float)qn[((int64_t)b * H + g * HPG + w) * kD + lane];
-  }
-  // ---- tile stream start --------------------------------------------------------
-  // Every wave issues its first two tiles here, at one program point: waves
-  // 0..HPG-1 after forming their absorbed query (so their prologue loads are
-  // not queued behind tiles they do not need yet), the other waves at once.
-  Tile<GQA, KR> X, Y;
-  issue(X, w);
-  issue(Y, w + kWaves);
-  // query slots past d_r contribute nothing (masked after the issue, so the
-  // wait for qr counts only the loads issued before it)
+  };
+
+  // GQA value rows of sub-tile st, channels 32*h + 8*r .. +7, from the stage
+  // (rows at or past the stored end read as zeros).
+  auto value_rows = [&](const Frags<DR>& T, int st, int h) {
+    const int row = 16 * st + col;
+    Frag f;
+    f.u = *reinterpret_cast<const u32x4*>(stage_w + 8192 + row * (kD * 2) + 16 * ((4 * h + r) ^ stage_swizzle(row)));
+    if (!T.full && T.t0 + row >= t_end) f.u = u32x4{0u, 0u, 0u, 0u};
+    return f;
+  };
+
+  // ---- queries --------------------------------------------------------------------
+  // query slots past d_r contribute nothing (masked after the tile issue, so
+  // the wait for qr counts only the loads issued before it)
   if constexpr (DR && !STEP) {
     if (8 * r >= d_r) qr.u = u32x4{0u, 0u, 0u, 0u};
+  }
+  if constexpr (!GQA) {
+    f32x4 D[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      D[m] = mma(mA[m][0], qB[0], kZero4);
+      D[m] = mma(mA[m][1], qB[1], D[m]);
+    }
+    // lane (col 0, group r) holds q'[32 * half + 8r + e] in D[e / 4][e % 4]
+    if (col == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qsh[gm_j][32 * gm_half + 8 * r + e] = D[e >> 2][e & 3];
+    }
+  } else {
+    if (gm_half == 0) qsh[gm_j][lane] = qv;
+  }
+  if constexpr (STEP) {
+    if (w == 0 && lane < 8) *reinterpret_cast<u32x4*>(vnew_sh + 8 * lane) = vnew_l;
   }
   if constexpr (STEP && DR) {
     if (rot_q || rot_k) {
@@ -367,29 +390,29 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       const double x1 = (double)__uint_as_float(rx & 0xffff0000u);
       const double at = rot_q ? (double)max(n_full - 1, 0) : (double)pos;
       double y0, y1;
-      rope_pair(x0, x1, at, theta_sh[rot_p], y0, y1);
+      rope_pair(x0, x1, at, rope_theta(a.rope, rot_p), y0, y1);
       __bf16* dst = rot_q ? &qrot_sh[rot_j][2 * rot_p] : &krot_sh[2 * rot_p];
       dst[0] = from_f64<__bf16>(y0);
       dst[1] = from_f64<__bf16>(y1);
     }
   }
   __syncthreads();
-  Frag qhi[2], qlo[2], knew;
+  // The second tile of every wave is requested only now: issued with the
+  // first it would hold this barrier (a wave stalls at load issue while the
+  // compute unit's request queue is full).
+  Tile<GQA, KR> Y;
+  issue(Y, w + kWaves, t_end, n_tiles);
+  // absorbed query as the bf16 B operand (accumulated in fp32, rounded once)
+  Frag qb[2];
 #pragma unroll
   for (int kc2 = 0; kc2 < 2; ++kc2) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = qsh[jcol][32 * kc2 + 8 * r + e];
-      const __bf16 hi = (__bf16)v;
-      qhi[kc2].h[e] = hi;
-      qlo[kc2].h[e] = (__bf16)(v - (float)hi);
-    }
+    for (int e = 0; e < 8; ++e) qb[kc2].h[e] = (__bf16)qsh[jcol][32 * kc2 + 8 * r + e];
   }
   if constexpr (STEP && DR) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       qr.h[e] = (8 * r < d_r) ? qrot_sh[jcol][kr_off + e] : (__bf16)0.f;
-      knew.h[e] = krot_sh[kr_off + e];
     }
   }
   // Fused step: split-0 workgroups store the appended token's rows.
@@ -407,12 +430,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
         krow = ((int64_t)b * a.capacity + pos) * d_r;
       }
       if (vrow >= 0) {
-        // lanes of column 0 hold channels 8r..8r+7 and 32+8r..32+8r+7 already
         __bf16* vdst = reinterpret_cast<__bf16*>(a.v_cache_rw) + vrow;
-        if (col == 0) {
-          *reinterpret_cast<u32x4*>(vdst + 8 * r) = vnew[0].u;
-          *reinterpret_cast<u32x4*>(vdst + 32 + 8 * r) = vnew[1].u;
-        }
+        if (lane < kD / 8) *reinterpret_cast<u32x4*>(vdst + 8 * lane) = *reinterpret_cast<const u32x4*>(vnew_sh + 8 * lane);
         if constexpr (DR) {
           if (g == 0 && lane < d_r / 8) {
             Frag kk;
@@ -443,17 +462,21 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   float m_ref = -INFINITY, l_run = 0.f;  // m_ref in raw score units
   const float thr = kRescaleLog2 / sl2;
 
-  auto process = [&](Frags<GQA, DR>& T) {
+  auto process = [&](Frags<DR>& T) {
     if (!T.ok) return;  // wave-uniform
     if constexpr (STEP) {
       // the appended row comes from the call's inputs, not from the cache
       if (has_new && pos >= T.t0 && pos < T.t0 + kTile) {
+        Frag v0, v1, kk;
+        v0.u = *reinterpret_cast<const u32x4*>(vnew_sh + 8 * r);
+        v1.u = *reinterpret_cast<const u32x4*>(vnew_sh + 32 + 8 * r);
+        if constexpr (DR) kk.u = *reinterpret_cast<const u32x4*>(krot_sh + kr_off);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           if (min(16 * st + col, T.bound) == pos - T.t0) {
-            T.sa[st][0] = vnew[0];
-            T.sa[st][1] = vnew[1];
-            if constexpr (DR) T.kr[st] = knew;
+            T.sa[st][0] = v0;
+            T.sa[st][1] = v1;
+            if constexpr (DR) T.kr[st] = kk;
           }
         }
       }
@@ -461,12 +484,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     f32x4 s[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      f32x4 c = mma(T.sa[st][0], qhi[0], kZero4);
-      c = mma(T.sa[st][1], qhi[1], c);
-      if constexpr (QLO) {
-        c = mma(T.sa[st][0], qlo[0], c);
-        c = mma(T.sa[st][1], qlo[1], c);
-      }
+      f32x4 c = mma(T.sa[st][0], qb[0], kZero4);
+      c = mma(T.sa[st][1], qb[1], c);
       if constexpr (DR) c = mma(T.kr[st], qr, c);
       s[st] = c;
     }
@@ -514,8 +533,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       for (int db = 0; db < 4; ++db) {
         f32x4 ca, cb;
         if constexpr (GQA) {
-          ca = mma(T.vb[2 * pr][db >> 1], sel[db & 1], kZero4);
-          cb = mma(T.vb[2 * pr + 1][db >> 1], sel[db & 1], kZero4);
+          ca = mma(value_rows(T, 2 * pr, db >> 1), sel[db & 1], kZero4);
+          cb = mma(value_rows(T, 2 * pr + 1, db >> 1), sel[db & 1], kZero4);
         } else {
           ca = mma(T.sa[2 * pr][db >> 1], sel[db & 1], kZero4);
           cb = mma(T.sa[2 * pr + 1][db >> 1], sel[db & 1], kZero4);
@@ -533,17 +552,23 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
 
   // Each tile is staged, its registers are reloaded at once with the tile
   // two rounds ahead, and the math runs on the staged copy.
-  Frags<GQA, DR> F;
+  // The loop has a single exit and issues both reloads on every path (a
+  // reload past the last tile reads row 0), so the compiler's wait counts for
+  // each tile stay exact across iterations.
+  Frags<DR> F;
+#pragma clang loop unroll(disable)
   for (int k = w; k < n_tiles; k += 2 * kWaves) {
     stage(X);
     fragments(F, X);
-    issue(X, k + 2 * kWaves);
+    issue(X, k + 2 * kWaves, t_end, n_tiles);
     process(F);
-    if (k + kWaves >= n_tiles) break;
-    stage(Y);
-    fragments(F, Y);
-    issue(Y, k + 3 * kWaves);
-    process(F);
+    const bool has_y = k + kWaves < n_tiles;  // wave-uniform
+    if (has_y) {
+      stage(Y);
+      fragments(F, Y);
+    }
+    issue(Y, k + 3 * kWaves, t_end, n_tiles);
+    if (has_y) process(F);
   }
 
   // ---- merge the waves ----------------------------------------------------------------

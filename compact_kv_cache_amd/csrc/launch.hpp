@@ -20,6 +20,21 @@ inline RopeTable make_rope_table(double base, int d_r) {
   return t;
 }
 
+// theta_i of pair i, selected per lane among the table's uniform values. The
+// empty asm statement keeps each value in a scalar register: without it the
+// compiler folds the selection into a lane-indexed read of the kernel
+// argument, a vector memory load that waits behind every load issued before.
+__device__ __forceinline__ double rope_theta(const RopeTable& t, int i) {
+  double th = 0.0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    double v = t.theta[k];
+    asm volatile("" : "+s"(v));
+    th = (i == k) ? v : th;
+  }
+  return th;
+}
+
 struct AppendLaunch {
   int B, G, d_r, n_new, capacity, num_blocks, max_blocks;
   bool paged, bf16;
