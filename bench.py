@@ -55,6 +55,9 @@ def parse():
                    help="only run N eager decodes (for rocprofv3 runs) and exit")
     p.add_argument("--profile-step", type=int, default=0,
                    help="only run N eager fused steps (for rocprofv3 runs) and exit")
+    p.add_argument("--profile-copy-mb", type=int, default=0,
+                   help="with --profile-step/--profile-decode: first run a plain elementwise copy "
+                        "(read N MiB, write N MiB) three times, the reference for traffic counters")
     p.add_argument("--mode", choices=["step", "gqa"], default="step")
     return p.parse_args()
 
@@ -160,6 +163,14 @@ def main():
         decode(r)
         step_bytes.append(wl.B * n_host[r] * bpt)
 
+    if args.profile_copy_mb and (args.profile_decode or args.profile_step):
+        nb = args.profile_copy_mb << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if args.profile_decode:
         for i in range(args.profile_decode):
             decode(i % R)
@@ -259,7 +270,7 @@ def main():
     # the timed region launches one kernel per step (the fused step)
     achieved = mean_step_bytes / (ms_step * 1e-3) / 1e9
 
-    traffic = None  # filled from profiles only while the kernel source matches (see design doc)
+    traffic = recorded_traffic(wl.name)
 
     result = {
         "metric": METRIC,
@@ -297,6 +308,32 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+KERNEL_SOURCES = ("compact_kv_cache_amd/csrc/decode_mfma.hip", "compact_kv_cache_amd/csrc/gva_device.hpp",
+                  "compact_kv_cache_amd/csrc/launch.hpp")
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per fused-step launch from the committed counter summary, or
+    None when there is none for this workload or the kernel sources changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"step_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].strip().split(": ", 1)
+            rec[k] = v
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    return int(rec["traffic_bytes_per_launch"])
 
 
 def gqa_compare(args):
