@@ -327,13 +327,24 @@ def recorded_traffic(workload: str):
         if line.startswith("- ") and ": " in line:
             k, v = line[2:].strip().split(": ", 1)
             rec[k] = v
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != h.hexdigest():
+    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return int(rec["traffic_bytes_per_launch"])
+
+
+def kernel_source_hash() -> str:
+    """sha256 of the decode kernel's sources with // comments, trailing blanks
+    and empty lines removed (comment edits do not change the kernel)."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f)) as fh:
+            for line in fh:
+                line = re.sub(r"//.*$", "", line).rstrip()
+                if line:
+                    h.update(line.encode() + b"\n")
+    return h.hexdigest()
 
 
 def gqa_compare(args):

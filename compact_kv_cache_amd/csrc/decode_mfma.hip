@@ -13,16 +13,22 @@
 //
 // Absorption prologue (GVA digest, 方法: Q' = Q M^T; explainer, 正式方案):
 // q'_h = M_h q_nope,h on MFMA (A = rows of M_h, B = q_nope,h in every
-// column), one (head, half of the contraction) per wave; M's rows are visited
-// in a permuted order so the product comes out directly in the score
-// operand's lane layout. M is read once per workgroup; waves without a query
-// to prepare start the cache-tile stream meanwhile.
+// column), split over all eight waves (half a head each); M's rows are
+// visited in a permuted order so the product comes out directly in the score
+// operand's lane layout.
+//
+// Tiles: every 16-byte load instruction of a wave covers 1 KB of contiguous
+// cache memory (8 whole V rows, or 1 KB of positional keys); the wave stores
+// the tile to its own LDS buffer (16-byte chunks XOR-swizzled per row) and
+// reads the matrix-core operands back from there. The first tile of every
+// wave is requested from the host bound max_seq_len, before the stored length
+// has arrived; rows past the stored end are cleared when the operands are read.
 //
 // Per wave and 16-token sub-tile, all on v_mfma_f32_16x16x32_bf16:
 //   scores     S^T[tok][col] = V[tok][:] . q'[head(col)][:] + k_r[tok] . q_rope:
-//              A = V rows exactly as loaded (lane l: token l%16, 8 channels),
-//              B = queries with the group's heads repeated across the 16
-//              columns; q' is accumulated in fp32 and rounded to bf16 once.
+//              A = V rows (lane l: token l%16, 8 channels), B = queries with
+//              the group's heads repeated across the 16 columns; q' is
+//              accumulated in fp32 and rounded to bf16 once.
 //   transpose  C[tok][c] = V[tok][:] . E[:][c], E a 0/1 selection of 16
 //              channels: V^T in the A layout of the next product, exactly.
 //   P.V        O^T[ch][col] += V^T[ch][tok] . P^T[tok][col] over 32 tokens; B =
@@ -31,10 +37,10 @@
 // and the raw v_exp_f32. The reference max m_ref only moves when a tile's max
 // exceeds it by more than 2^8 in probability units, so the output rescale is
 // rare and p stays below 256.
-// Cache tiles are read with non-temporal loads from a wave-uniform tile base
-// plus per-lane offsets; rows past the end are clamped, a missing tile reads
-// the first row, so no load is ever predicated and the next tile's loads stay
-// in flight while the current one is computed.
+// Loads are non-temporal, from a wave-uniform tile base plus per-lane offsets;
+// rows past the end are clamped and a missing page reads the first row, so no
+// load is ever predicated and the next tile's loads stay in flight while the
+// current one is computed.
 //
 // Fused step (the decode loop of the GQA tutorial page, section on cache
 // growth: store the new token's state, then let its query read the cache up to
@@ -42,10 +48,9 @@
 // positional key and the query slice are rotated in the prologue with the same
 // double-precision routine as gva_append / gva_rope_query, split-0 workgroups
 // store the new rows, and the workgroup whose tile holds the new position
-// substitutes that row in registers. Every workgroup of the sequence takes a
-// ticket after reading seq_lens[b]; the last ticket stores the new length, so
-// no workgroup can observe it mid-call. Results equal the three separate
-// calls bit for bit.
+// substitutes that row. Every workgroup of the sequence takes a ticket after
+// reading seq_lens[b]; the last ticket stores the new length, so no workgroup
+// can observe it mid-call. Results equal the three separate calls bit for bit.
 #include "gva_device.hpp"
 #include "launch.hpp"
 
