@@ -49,11 +49,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendLaunch a, CacheGeom c
       const int64_t dst = kr_row<PAGED>(c, b, pos);
       if (dst < 0) continue;
       const int64_t src = ((int64_t)b * a.n_new + t) * a.d_r + 2 * p;
-      double y0, y1;
-      rope_pair((double)to_f32(ksrc[src]), (double)to_f32(ksrc[src + 1]), (double)pos, a.rope.theta[p],
-                y0, y1);
-      kdst[dst + 2 * p] = from_f64<T>(y0);
-      kdst[dst + 2 * p + 1] = from_f64<T>(y1);
+      rope_store<T>(to_f32(ksrc[src]), to_f32(ksrc[src + 1]), (double)pos, a.rope.theta[p], kdst[dst + 2 * p],
+                    kdst[dst + 2 * p + 1]);
     }
   }
 
@@ -78,10 +75,10 @@ __global__ __launch_bounds__(256) void rope_query_kernel(RopeQueryLaunch a) {
   for (int i = threadIdx.x; i < a.H * half; i += blockDim.x) {
     const int h = i / half, p = i % half;
     const int64_t off = ((int64_t)b * a.H + h) * a.d_r + 2 * p;
-    double y0, y1;
-    rope_pair((double)to_f32(src[off]), (double)to_f32(src[off + 1]), pos, a.rope.theta[p], y0, y1);
-    dst[off] = from_f64<T>(y0);
-    dst[off + 1] = from_f64<T>(y1);
+    T y0, y1;  // (the rotation may be in place)
+    rope_store<T>(to_f32(src[off]), to_f32(src[off + 1]), pos, a.rope.theta[p], y0, y1);
+    dst[off] = y0;
+    dst[off + 1] = y1;
   }
 }
 

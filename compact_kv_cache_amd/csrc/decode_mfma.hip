@@ -46,7 +46,7 @@
 // growth: store the new token's state, then let its query read the cache up to
 // and including itself): the appended position is the old seq_lens[b]; the
 // positional key and the query slice are rotated in the prologue with the same
-// double-precision routine as gva_append / gva_rope_query, split-0 workgroups
+// routine as gva_append / gva_rope_query, split-0 workgroups
 // store the new rows, and the workgroup whose tile holds the new position
 // substitutes that row. Every workgroup of the sequence takes a ticket after
 // reading seq_lens[b]; the last ticket stores the new length, so no workgroup
@@ -391,14 +391,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   }
   if constexpr (STEP && DR) {
     if (rot_q || rot_k) {
-      const double x0 = (double)__uint_as_float(rx << 16);
-      const double x1 = (double)__uint_as_float(rx & 0xffff0000u);
+      const float x0 = __uint_as_float(rx << 16);
+      const float x1 = __uint_as_float(rx & 0xffff0000u);
       const double at = rot_q ? (double)max(n_full - 1, 0) : (double)pos;
-      double y0, y1;
-      rope_pair(x0, x1, at, rope_theta(a.rope, rot_p), y0, y1);
       __bf16* dst = rot_q ? &qrot_sh[rot_j][2 * rot_p] : &krot_sh[2 * rot_p];
-      dst[0] = from_f64<__bf16>(y0);
-      dst[1] = from_f64<__bf16>(y1);
+      rope_store<__bf16>(x0, x1, at, rope_theta(a.rope, rot_p), dst[0], dst[1]);
     }
   }
   __syncthreads();

@@ -34,16 +34,63 @@ template <> __device__ __forceinline__ __bf16 from_f64<__bf16>(double x) {
 }
 
 // ---------------------------------------------------------------------------
-// RoPE on one channel pair (2i, 2i+1) at position pos: counter-clockwise turn
-// by pos * theta_i (theta_i = base^(-2i/d_r), precomputed), in double
-// precision.
+// Sine and cosine of a >= 0 in double precision, for the RoPE angles
+// (a = pos * theta_i <= 2^32). Cody-Waite reduction by pi/2 split into two
+// doubles (k * hi is exact in the fused multiply-add, and the dropped third
+// part times k stays below 1e-28), so r = a - k*pi/2 lies in [-pi/4, pi/4]
+// up to rounding; then the Taylor series of sin to r^15 and cos to r^16,
+// whose first omitted terms are below 5e-17 there; then the quadrant k mod 4.
+// Straight-line code: no large-argument path, no table.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void sincos_angle(double a, double& s, double& c) {
+  constexpr double kTwoOverPi = 0.6366197723675814;
+  constexpr double kPiO2Hi = 1.5707963267948966;     // pi/2 rounded to double
+  constexpr double kPiO2Mid = 6.123233995736766e-17;  // pi/2 - kPiO2Hi, rounded
+  const double k = rint(a * kTwoOverPi);
+  const double r = fma(-k, kPiO2Mid, fma(-k, kPiO2Hi, a));
+  const double r2 = r * r;
+  // coefficients 1/n!
+  double ps = -7.647163731819816e-13;              // -1/15!
+  ps = fma(ps, r2, 1.6059043836821613e-10);        //  1/13!
+  ps = fma(ps, r2, -2.505210838544172e-08);        // -1/11!
+  ps = fma(ps, r2, 2.7557319223985893e-06);        //  1/9!
+  ps = fma(ps, r2, -0.0001984126984126984);        // -1/7!
+  ps = fma(ps, r2, 0.008333333333333333);          //  1/5!
+  ps = fma(ps, r2, -0.16666666666666666);          // -1/3!
+  const double sr = fma(r * r2, ps, r);
+  double pc = 4.779477332387385e-14;               //  1/16!
+  pc = fma(pc, r2, -1.1470745597729725e-11);       // -1/14!
+  pc = fma(pc, r2, 2.08767569878681e-09);          //  1/12!
+  pc = fma(pc, r2, -2.755731922398589e-07);        // -1/10!
+  pc = fma(pc, r2, 2.48015873015873e-05);          //  1/8!
+  pc = fma(pc, r2, -0.001388888888888889);         // -1/6!
+  pc = fma(pc, r2, 0.041666666666666664);          //  1/4!
+  pc = fma(pc, r2, -0.5);                          // -1/2!
+  const double cr = fma(r2, pc, 1.0);
+  const int q = (int)((long long)k & 3);
+  const double s0 = (q & 1) ? cr : sr;
+  const double c0 = (q & 1) ? sr : cr;
+  s = (q & 2) ? -s0 : s0;
+  c = ((q + 1) & 2) ? -c0 : c0;
+}
+
+// RoPE on one channel pair (2i, 2i+1) at position pos: counter-clockwise turn
+// by pos * theta_i (theta_i = base^(-2i/d_r), precomputed on the host), in
+// double precision.
 __device__ __forceinline__ void rope_pair(double x0, double x1, double pos, double theta,
                                           double& y0, double& y1) {
   double s, c;
-  sincos(pos * theta, &s, &c);
+  sincos_angle(pos * theta, s, c);
   y0 = x0 * c - x1 * s;
   y1 = x0 * s + x1 * c;
+}
+// Rotate a stored pair and round it to the storage type T.
+template <typename T>
+__device__ __forceinline__ void rope_store(float x0, float x1, double pos, double theta, T& y0, T& y1) {
+  double a, b;
+  rope_pair((double)x0, (double)x1, pos, theta, a, b);
+  y0 = from_f64<T>(a);
+  y1 = from_f64<T>(b);
 }
 
 // ---------------------------------------------------------------------------
