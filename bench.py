@@ -58,7 +58,7 @@ def parse():
     p.add_argument("--profile-copy-mb", type=int, default=0,
                    help="with --profile-step/--profile-decode: first run a plain elementwise copy "
                         "(read N MiB, write N MiB) three times, the reference for traffic counters")
-    p.add_argument("--mode", choices=["step", "gqa"], default="step")
+    p.add_argument("--mode", choices=["step", "gqa", "folded"], default="step")
     return p.parse_args()
 
 
@@ -84,6 +84,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.mode == "gqa":
         gqa_compare(args)
+        return
+    if args.mode == "folded":
+        folded_compare(args)
         return
     wl = W.WORKLOADS[args.workload]
     if args.split >= 0:
@@ -305,6 +308,18 @@ def main():
                      "bytes_per_launch": mean_step_bytes},
     }
 
+    if use_graph:
+        # speed-up of the decode over the same-shape GQA reference (decode
+        # kernels only, each timed back to back over its own cold replicas)
+        caches.clear()  # the step replicas are no longer needed
+        Ms.clear()
+        torch.cuda.empty_cache()
+        cmp = measure_gva_vs_gqa(wl, K)
+        result["gqa_decode_us"] = cmp["gqa"]["us"]
+        result["gva_decode_us_same_pass"] = cmp["gva"]["us"]
+        result["speedup_vs_gqa"] = cmp["time_ratio_gqa_over_gva"]
+        result["gqa_byte_ratio"] = cmp["byte_ratio_gqa_over_gva"]
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -348,6 +363,123 @@ def kernel_source_hash() -> str:
 
 
 def gqa_compare(args):
+    """`--mode gqa`: gva_decode against gva_gqa_ref_decode on the wide workload
+    (or the one named), one JSON line."""
+    import workloads as W
+    wl = W.WORKLOADS["wide_dr24" if args.workload == "mid_bf16" else args.workload]
+    res = measure_gva_vs_gqa(wl, args.steps)
+    res["config"] = {"workload": f"{wl.name}: B={wl.B} S={wl.S} H={wl.H} G={wl.G} d_v={wl.d_v} "
+                                 f"d_r={wl.d_r} {wl.dtype}, contiguous caches, cold replicas",
+                     "steps": args.steps}
+    print(json.dumps(res), flush=True)
+
+
+def folded_compare(args):
+    """`--mode folded`: one layer's decode step from hidden states x [B, d_model]
+    (d_model = H * d_n), with and without the maps folded into the query
+    projection. unfolded: projection to q_nope, q_rope, then the fused step
+    with M; folded: projection to q' = (M W_q,nope) x, q_rope, then the fused
+    step without M. Every replica (layer) has its own weights and cache; each
+    variant is timed as K steps in one graph."""
+    import numpy as np
+    import torch
+
+    import compact_kv_cache_amd as gva
+    import workloads as W
+    from compact_kv_cache_amd.cache import GvaCache
+
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS[args.workload]
+    K = args.steps
+    d_model = wl.H * wl.d_n
+    bpt = gva.gva_cache_bytes_per_token(wl.G, wl.d_v, wl.d_r, wl.dtype)
+    R = max(2, math.ceil(512e6 / (wl.B * wl.S * bpt)))
+    n_steps = 6 * K + 8
+    cap = wl.S + math.ceil(n_steps / R) + 2
+    inp = W.make_gva_inputs(wl)
+    to = lambda a: W.to_torch(a, wl.dtype).to(dev)  # noqa: E731
+    first = GvaCache(wl.B, wl.H, wl.G, wl.d_n, wl.d_v, wl.d_r, dtype=wl.dtype, capacity=cap, device=dev)
+    first.append(to(np.stack(inp.V)), to(np.stack(inp.kr)), wl.rope_base)
+    caches = [first]
+    for _ in range(R - 1):
+        c = GvaCache(wl.B, wl.H, wl.G, wl.d_n, wl.d_v, wl.d_r, dtype=wl.dtype, capacity=cap, device=dev)
+        c.v_cache.copy_(first.v_cache)
+        c.kr_cache.copy_(first.kr_cache)
+        c.seq_lens.copy_(first.seq_lens)
+        caches.append(c)
+    x_h, wq_nope_h, wq_rope_h = W.make_projection_inputs(wl, d_model)
+    M = to(inp.M)
+    layers = []
+    for r in range(R):
+        wq = to(wq_nope_h) if r == 0 else layers[0]["wq"].clone()
+        wr = to(wq_rope_h) if r == 0 else layers[0]["wr"].clone()
+        wf = torch.empty(wl.H, wl.d_v, d_model, dtype=W.torch_dtype(wl.dtype), device=dev)
+        gva.gva_fold_query_projection(M, wq, wf)
+        layers.append({"wq": wq, "wr": wr, "wf": wf, "M": M.clone()})
+    del inp
+    x = to(x_h)
+    td = W.torch_dtype(wl.dtype)
+    q_a = torch.empty(wl.B, wl.H, wl.d_v, dtype=td, device=dev)
+    q_r = torch.empty(wl.B, wl.H, wl.d_r, dtype=td, device=dev)
+    out = torch.empty(wl.B, wl.H, wl.d_v, dtype=td, device=dev)
+    v_new = torch.randn(wl.B, wl.G, wl.d_v, device=dev).to(td)
+    k_new = torch.randn(wl.B, wl.d_r, device=dev).to(td)
+    n_host = [wl.S] * R
+    ws = torch.zeros(gva.gva_decode_step_workspace_bytes(caches[0].shape(cap)) // 4 + 1,
+                     dtype=torch.float32, device=dev)
+
+    def project(i, folded):
+        r = i % R
+        L = layers[r]
+        gva.gva_query_projection(caches[r].shape(cap), x, L["wf"] if folded else L["wq"], L["wr"], q_a, q_r)
+
+    def fstep(i, folded):
+        r = i % R
+        n_host[r] += 1
+        caches[r].step(v_new, k_new, q_a, q_r, None if folded else layers[r]["M"], wl.scale, out, n_host[r],
+                       workspace=ws, rope_base=wl.rope_base)
+
+    def layer_step(i, folded):
+        project(i, folded)
+        fstep(i, folded)
+
+    def gtime(fn, first_i):
+        for k in range(2 * R):
+            fn(first_i + k)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(K):
+                fn(first_i + 2 * R + k)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K * 1e3
+
+    # lengths grow by one per step and replica; every variant steps the same caches
+    res = {}
+    res["unfolded_layer_step_us"] = gtime(lambda i: layer_step(i, False), 0)
+    res["folded_layer_step_us"] = gtime(lambda i: layer_step(i, True), 0)
+    res["fused_step_with_M_us"] = gtime(lambda i: fstep(i, False), 0)
+    res["fused_step_folded_us"] = gtime(lambda i: fstep(i, True), 0)
+    res["projection_us"] = gtime(lambda i: project(i, True), 0)
+    res = {k: round(v, 3) for k, v in res.items()}
+    res.update({
+        "mode": "folded_compare",
+        "config": {"workload": f"{wl.name}: B={wl.B} S={wl.S}.. H={wl.H} G={wl.G} d_v=d_n={wl.d_v} "
+                               f"d_r={wl.d_r} d_model={d_model} {wl.dtype}, {R} cold replicas with their own "
+                               f"weights", "steps": K},
+        "layer_steps_per_s": {"unfolded": round(1e6 / res["unfolded_layer_step_us"], 1),
+                              "folded": round(1e6 / res["folded_layer_step_us"], 1)},
+        "projection_weight_bytes": wl.H * (wl.d_v + wl.d_r) * d_model * 2,
+    })
+    print(json.dumps(res), flush=True)
+
+
+def measure_gva_vs_gqa(wl, K: int) -> dict:
     """gva_decode and gva_gqa_ref_decode on the same B, S, G, H and d_v = d_h:
     the GVA cache (G value rows + one positional key per token) against the
     GQA cache (G key rows + G value rows per token). Each is timed as K
@@ -356,11 +488,8 @@ def gqa_compare(args):
     import torch
 
     import compact_kv_cache_amd as gva
-    import workloads as W
 
     dev = torch.device("cuda:0")
-    wl = W.WORKLOADS["wide_dr24" if args.workload == "mid_bf16" else args.workload]
-    K = args.steps
     out = {}
     for kind in ("gva", "gqa"):
         d_r = wl.d_r if kind == "gva" else 0
@@ -410,14 +539,9 @@ def gqa_compare(args):
                      "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4), "replicas": R}
         del reps
         torch.cuda.empty_cache()
-    res = {"mode": "gqa_compare",
-           "config": {"workload": f"{wl.name}: B={wl.B} S={wl.S} H={wl.H} G={wl.G} d_v={wl.d_v} "
-                                  f"d_r={wl.d_r} {wl.dtype}, contiguous caches, cold replicas",
-                      "steps": K},
-           "gva": out["gva"], "gqa": out["gqa"],
-           "time_ratio_gqa_over_gva": round(out["gqa"]["us"] / out["gva"]["us"], 3),
-           "byte_ratio_gqa_over_gva": round(out["gqa"]["bytes"] / out["gva"]["bytes"], 3)}
-    print(json.dumps(res), flush=True)
+    return {"mode": "gqa_compare", "gva": out["gva"], "gqa": out["gqa"],
+            "time_ratio_gqa_over_gva": round(out["gqa"]["us"] / out["gva"]["us"], 3),
+            "byte_ratio_gqa_over_gva": round(out["gqa"]["bytes"] / out["gva"]["bytes"], 3)}
 
 
 def cpu_baseline(wl, seconds: float):

@@ -17,6 +17,7 @@ from ._lib import GVA_BF16, GVA_F32, GvaShape
 __all__ = [
     "GvaShape", "GVA_F32", "GVA_BF16", "GvaError", "make_shape", "lib",
     "gva_append", "gva_rope_query", "gva_decode", "gva_decode_step", "gva_gqa_ref_decode",
+    "gva_fold_query_projection", "gva_query_projection",
     "gva_decode_workspace_bytes", "gva_decode_step_workspace_bytes", "gva_decode_split_tokens", "gva_cache_bytes_per_token",
     "gva_status_string", "gva_abi_version", "workspace_for",
 ]
@@ -111,6 +112,36 @@ def gva_decode_step(shape: GvaShape, v_new, kr_new, q_nope, q_rope, M, v_cache, 
                                float(rope_base), _ptr(out, dt, "out"),
                                _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream)),
            "gva_decode_step")
+
+
+def gva_fold_query_projection(M, wq_nope, w_fold, stream=None) -> None:
+    """w_fold[h] = M[h] @ wq_nope[h]: M [H, d_v, d_n], wq_nope [H, d_n, d_model],
+    w_fold [H, d_v, d_model], all of one dtype (bf16 or fp32)."""
+    if M.dim() != 3 or wq_nope.dim() != 3 or w_fold.dim() != 3:
+        raise ValueError("M, wq_nope and w_fold must be 3-D")
+    H, d_v, d_n = M.shape
+    d_model = wq_nope.shape[2]
+    if tuple(wq_nope.shape) != (H, d_n, d_model) or tuple(w_fold.shape) != (H, d_v, d_model):
+        raise ValueError(f"shapes M {tuple(M.shape)}, wq_nope {tuple(wq_nope.shape)}, "
+                         f"w_fold {tuple(w_fold.shape)} do not match")
+    code = {torch.bfloat16: 1, torch.float32: 0}.get(M.dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {M.dtype}")
+    _check(lib.gva_fold_query_projection(H, d_v, d_n, d_model, code, _ptr(M, M.dtype, "M"),
+                                         _ptr(wq_nope, M.dtype, "wq_nope"),
+                                         _ptr(w_fold, M.dtype, "w_fold"), _stream(stream)),
+           "gva_fold_query_projection")
+
+
+def gva_query_projection(shape: GvaShape, x, w_fold, w_rope, q_abs, q_rope, stream=None) -> None:
+    """q_abs = w_fold . x and q_rope = w_rope . x (pre-RoPE) for the B new tokens:
+    x [B, d_model], w_fold [H, d_v, d_model], w_rope [H, d_r, d_model]."""
+    dt = _TORCH.get(shape.dtype)
+    d_model = x.shape[-1]
+    _check(lib.gva_query_projection(shape, int(d_model), _ptr(x, dt, "x"), _ptr(w_fold, dt, "w_fold"),
+                                    _ptr(w_rope, dt, "w_rope"), _ptr(q_abs, dt, "q_abs"),
+                                    _ptr(q_rope, dt, "q_rope"), _stream(stream)),
+           "gva_query_projection")
 
 
 def gva_gqa_ref_decode(shape: GvaShape, q, k_cache, v_cache, seq_lens, block_table, scale: float,

@@ -202,8 +202,8 @@ gva_status gva_decode(const gva_shape* shape, const void* q_nope, const void* q_
                       size_t workspace_bytes, hipStream_t stream) {
   gva_status st = check_shape(shape, false);
   if (st != GVA_OK) return st;
-  if (!q_nope || !M || !v_cache || !seq_lens || !out)
-    return fail(GVA_ERR_INVALID_ARGUMENT, "q_nope, M, v_cache, seq_lens and out must be non-NULL");
+  if (!q_nope || !v_cache || !seq_lens || !out)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "q_nope, v_cache, seq_lens and out must be non-NULL");
   if (shape->d_r > 0 && (!q_rope || !kr_cache))
     return fail(GVA_ERR_INVALID_ARGUMENT, "q_rope and kr_cache must be non-NULL when d_r > 0");
   if (shape->block_size != 0 && !block_table)
@@ -237,8 +237,8 @@ gva_status gva_decode_step(const gva_shape* shape, const void* v_new, const void
                            hipStream_t stream) {
   gva_status st = check_shape(shape, false);
   if (st != GVA_OK) return st;
-  if (!v_new || !q_nope || !M || !v_cache || !seq_lens || !out)
-    return fail(GVA_ERR_INVALID_ARGUMENT, "v_new, q_nope, M, v_cache, seq_lens and out must be non-NULL");
+  if (!v_new || !q_nope || !v_cache || !seq_lens || !out)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "v_new, q_nope, v_cache, seq_lens and out must be non-NULL");
   if (shape->d_r > 0 && (!kr_new || !q_rope || !kr_cache))
     return fail(GVA_ERR_INVALID_ARGUMENT, "kr_new, q_rope and kr_cache must be non-NULL when d_r > 0");
   if (shape->block_size != 0 && !block_table)
@@ -324,6 +324,39 @@ gva_status gva_decode_step(const gva_shape* shape, const void* v_new, const void
     e = gva::launch_decode_valu(a, stream);
   }
   return hip_status(e, "gva_decode_step launch");
+}
+
+gva_status gva_fold_query_projection(int32_t H, int32_t d_v, int32_t d_n, int32_t d_model, int32_t dtype,
+                                     const void* M, const void* wq_nope, void* w_fold, hipStream_t stream) {
+  if (H < 1 || d_model < 1) return fail(GVA_ERR_INVALID_ARGUMENT, "H and d_model must be >= 1");
+  if (d_v != 64 || d_n != 64)
+    return fail(GVA_ERR_UNSUPPORTED, "d_n = %d, d_v = %d; built for d_n = d_v = 64", d_n, d_v);
+  if (dtype != GVA_F32 && dtype != GVA_BF16)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "dtype %d is not a gva_dtype", dtype);
+  if (!M || !wq_nope || !w_fold)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "M, wq_nope and w_fold must be non-NULL");
+  if ((int64_t)H * d_v * d_model > INT32_MAX)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "H * d_v * d_model too large");
+  gva::FoldLaunch a{H, d_v, d_n, d_model, dtype == GVA_BF16, M, wq_nope, w_fold};
+  return hip_status(gva::launch_fold(a, stream), "gva_fold_query_projection launch");
+}
+
+gva_status gva_query_projection(const gva_shape* shape, int32_t d_model, const void* x, const void* w_fold,
+                                const void* w_rope, void* q_abs, void* q_rope, hipStream_t stream) {
+  gva_status st = check_shape(shape, false);
+  if (st != GVA_OK) return st;
+  if (d_model < 1) return fail(GVA_ERR_INVALID_ARGUMENT, "d_model must be >= 1");
+  if (shape->dtype == GVA_BF16 && d_model % 128 != 0)
+    return fail(GVA_ERR_UNSUPPORTED, "bf16 projection needs d_model %% 128 == 0 (got %d)", d_model);
+  if (!x || !w_fold || !q_abs) return fail(GVA_ERR_INVALID_ARGUMENT, "x, w_fold and q_abs must be non-NULL");
+  if (shape->d_r > 0 && (!w_rope || !q_rope))
+    return fail(GVA_ERR_INVALID_ARGUMENT, "w_rope and q_rope must be non-NULL when d_r > 0");
+  if ((int64_t)shape->H * (shape->d_v + shape->d_r) * d_model > INT32_MAX ||
+      (int64_t)shape->B * d_model > INT32_MAX)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "projection too large");
+  gva::ProjectLaunch a{shape->B, shape->H, shape->d_v, shape->d_r, d_model, shape->dtype == GVA_BF16,
+                       x, w_fold, w_rope, q_abs, q_rope};
+  return hip_status(gva::launch_project(a, stream), "gva_query_projection launch");
 }
 
 size_t gva_decode_step_workspace_bytes(const gva_shape* shape) {

@@ -163,8 +163,13 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   const int gm_j = (w & 3) % HPG, gm_half = w >> 2;
   const int h_w = g * HPG + gm_j;
   Frag mA[2][2], qB[2];
-  float qv = 0.f;
-  if constexpr (!GQA) {
+  uint32_t qv_bits = 0;  // folded or GQA query element (bf16 bits), converted after the tile issue
+  // M == nullptr: the query projection already carries the reconstruction
+  // map (GVA digest, section 与现有产品 / 工作流的接口: the map can be folded
+  // into the query projection), so q_nope holds q' = M_h q_nope,h itself and
+  // is used as loaded, like a GQA query.
+  const bool folded = GQA || a.M == nullptr;  // wave-uniform
+  if (!folded) {
     const __bf16* Mh = reinterpret_cast<const __bf16*>(a.M) + (int64_t)h_w * kD * kD;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -175,9 +180,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     }
 #pragma unroll
     for (int kc2 = 0; kc2 < 2; ++kc2) qB[kc2].u = ld16(qn + ((int64_t)b * H + h_w) * kD, 32 * kc2 + 8 * r);
-  } else {
-    qv = (float)qn[((int64_t)b * H + h_w) * kD + lane];
   }
+  // (loaded in every mode, so that no wave waits for it inside a branch)
+  qv_bits = reinterpret_cast<const uint16_t*>(qn)[((int64_t)b * H + h_w) * kD + lane];
   Frag qr;
   if constexpr (DR && !STEP)
     qr.u = ld16(reinterpret_cast<const __bf16*>(a.q_rope) + ((int64_t)b * H + h_col) * d_r, kr_off);
@@ -371,7 +376,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   if constexpr (DR && !STEP) {
     if (8 * r >= d_r) qr.u = u32x4{0u, 0u, 0u, 0u};
   }
-  if constexpr (!GQA) {
+  if (!folded) {
     f32x4 D[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -384,7 +389,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       for (int e = 0; e < 8; ++e) qsh[gm_j][32 * gm_half + 8 * r + e] = D[e >> 2][e & 3];
     }
   } else {
-    if (gm_half == 0) qsh[gm_j][lane] = qv;
+    if (gm_half == 0) qsh[gm_j][lane] = __uint_as_float(qv_bits << 16);
   }
   if constexpr (STEP) {
     if (w == 0 && lane < 8) *reinterpret_cast<u32x4*>(vnew_sh + 8 * lane) = vnew_l;

@@ -40,12 +40,18 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeLaunch a) {
   const float sl2 = a.scale * kLog2e;
   const int h = g * HPG + w;  // head of this wave (valid when w < HPG)
 
-  // Absorption prologue: thread (w, lane) forms q'[w][d = lane].
+  // Absorption prologue: thread (w, lane) forms q'[w][d = lane]. With M ==
+  // nullptr the maps are folded into the query projection and q_nope already
+  // holds q'.
   if (w < HPG) {
-    const T* Mh = reinterpret_cast<const T*>(a.M) + ((int64_t)h * kD + lane) * kD;
     const T* qn = reinterpret_cast<const T*>(a.q_nope) + ((int64_t)b * H + h) * kD;
     float acc = 0.f;
-    for (int j = 0; j < kD; ++j) acc = fmaf(to_f32(Mh[j]), to_f32(qn[j]), acc);
+    if (a.M) {
+      const T* Mh = reinterpret_cast<const T*>(a.M) + ((int64_t)h * kD + lane) * kD;
+      for (int j = 0; j < kD; ++j) acc = fmaf(to_f32(Mh[j]), to_f32(qn[j]), acc);
+    } else {
+      acc = to_f32(qn[lane]);
+    }
     qs[w][lane] = acc * sl2;
     if (lane < d_r)
       qrs[w][lane] = to_f32(reinterpret_cast<const T*>(a.q_rope)[((int64_t)b * H + h) * d_r + lane]) * sl2;

@@ -104,6 +104,30 @@ inline size_t ws_step_bytes(int B, int H, int G, int n_split) {
   return ws_counter_bytes(B, G) + ws_partial_bytes(B, H, n_split) + ws_qrot_bytes(B, H);
 }
 
+// Offline fold of the reconstruction maps into the query projection:
+// w_fold[h] = M[h] (d_v x d_n) . wq[h] (d_n x d_model).
+struct FoldLaunch {
+  int H, d_v, d_n, d_model;
+  bool bf16;
+  const void* M;
+  const void* wq;
+  void* w_fold;
+};
+
+// Query projection from hidden states: rows 0 .. H*d_v-1 of the output are
+// w_fold . x (q' per head), rows H*d_v .. H*(d_v+d_r)-1 are w_rope . x.
+struct ProjectLaunch {
+  int B, H, d_v, d_r, d_model;
+  bool bf16;
+  const void* x;       // [B][d_model]
+  const void* w_fold;  // [H][d_v][d_model]
+  const void* w_rope;  // [H][d_r][d_model] (unused when d_r == 0)
+  void* q_abs;         // [B][H][d_v]
+  void* q_rope;        // [B][H][d_r]
+};
+
+hipError_t launch_fold(const FoldLaunch& a, hipStream_t s);
+hipError_t launch_project(const ProjectLaunch& a, hipStream_t s);
 hipError_t launch_append(const AppendLaunch& a, hipStream_t s);
 hipError_t launch_rope_query(const RopeQueryLaunch& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeLaunch& a, hipStream_t s);

@@ -148,7 +148,11 @@ gva_status gva_rope_query(const gva_shape* shape, const void* q_rope_in, void* q
  *   q_nope   [B][H][d_n]      content slice of the queries
  *   q_rope   [B][H][d_r]      positional slice, ALREADY rotated (see
  *                             gva_rope_query); NULL allowed when d_r == 0
- *   M        [H][d_v][d_n]    reconstruction maps (K_h = V_g(h) M_h)
+ *   M        [H][d_v][d_n]    reconstruction maps (K_h = V_g(h) M_h), or NULL:
+ *                             then q_nope holds the absorbed queries
+ *                             q'[b,h] = M_h q_nope[b,h] themselves, [B][H][d_v]
+ *                             (the maps folded into the query projection, see
+ *                             gva_fold_query_projection), used as given
  *   v_cache, kr_cache, block_table   as described at gva_shape
  *   seq_lens int32 [B]        tokens to attend (the query's own included)
  *   scale    softmax scale, finite and > 0 (e.g. 1/sqrt(d_n + d_r))
@@ -181,7 +185,8 @@ gva_status gva_decode(const gva_shape* shape, const void* q_nope, const void* q_
  * kernel launch; for fp32 the library runs the three kernels in sequence.
  *   v_new    [B][G][d_v]     values of the new token
  *   kr_new   [B][d_r]        its positional key BEFORE RoPE
- *   q_nope   [B][H][d_n]     query content slice
+ *   q_nope   [B][H][d_n]     query content slice ([B][H][d_v] absorbed queries
+ *                            when M is NULL, as for gva_decode)
  *   q_rope   [B][H][d_r]     query positional slice BEFORE RoPE (not modified)
  *   seq_lens int32 [B], in/out: the new token lands at seq_lens[b] and the
  *            value grows by one (clamped to the capacity as in gva_append)
@@ -199,6 +204,38 @@ gva_status gva_decode_step(const gva_shape* shape, const void* v_new, const void
 /* Bytes of device workspace gva_decode_step needs (never 0 for a valid
  * shape). Returns 0 for an invalid shape. */
 size_t gva_decode_step_workspace_bytes(const gva_shape* shape);
+
+/*
+ * gva_fold_query_projection - fold the reconstruction maps into the query
+ * projection, once per model ([digest] section 与现有产品 / 工作流的接口: at
+ * inference the reconstruction matrix can be folded into the query projection
+ * and content keys are never formed; the absorption itself is Q' = Q M^T,
+ * [digest] 方法). With q_nope[h] = wq_nope[h] . x,
+ *   w_fold[h] = M[h] . wq_nope[h]       so that   M_h q_nope,h = w_fold[h] . x
+ *   M        [H][d_v][d_n]
+ *   wq_nope  [H][d_n][d_model]   content rows of the query projection
+ *   w_fold   [H][d_v][d_model]   output, dtype; fp32 accumulation, rounded once
+ * d_v = d_n = 64; d_model >= 1. All pointers are device pointers.
+ */
+gva_status gva_fold_query_projection(int32_t H, int32_t d_v, int32_t d_n, int32_t d_model, int32_t dtype,
+                                     const void* M, const void* wq_nope, void* w_fold, hipStream_t stream);
+
+/*
+ * gva_query_projection - the decode queries of one layer from its hidden
+ * states, with the maps already folded:
+ *   q_abs[b][h]  = w_fold[h] . x[b]    absorbed content queries (pass as
+ *                                      q_nope with M = NULL)
+ *   q_rope[b][h] = w_rope[h] . x[b]    positional slices BEFORE RoPE
+ *   x        [B][d_model]        hidden states of the new tokens
+ *   w_fold   [H][d_v][d_model]   from gva_fold_query_projection
+ *   w_rope   [H][d_r][d_model]   positional rows of the query projection
+ *                                (NULL when d_r == 0, and then q_rope too)
+ *   q_abs    [B][H][d_v], q_rope [B][H][d_r]   outputs in the call dtype
+ * Uses B, H, G, d_v, d_r and dtype of `shape`. fp32 accumulation; bf16 runs on
+ * the matrix cores and needs d_model % 128 == 0.
+ */
+gva_status gva_query_projection(const gva_shape* shape, int32_t d_model, const void* x, const void* w_fold,
+                                const void* w_rope, void* q_abs, void* q_rope, hipStream_t stream);
 
 /*
  * gva_gqa_ref_decode - plain grouped-query attention decode over a K+V cache

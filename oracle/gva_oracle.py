@@ -233,6 +233,38 @@ def gva_decode_step(V, kr_pre, q_nope, q_rope_pre, M, seq_lens, scale: float,
     return gva_decode(V, kr_rot, q_nope, q_rot, M, seq_lens, scale)
 
 
+# ---------------------------------------------------------------------------
+# The query projection, and the maps folded into it ([digest] 与现有产品 /
+# 工作流的接口: at inference the reconstruction matrix can be folded into the
+# query projection, so content keys are never formed)
+# ---------------------------------------------------------------------------
+
+def query_projection(x, w) -> np.ndarray:
+    """Per-head linear projection of hidden states: w [H, d, d_model] applied
+    to x [B, d_model] gives [B, H, d] (q[b, h] = w[h] @ x[b]), float64."""
+    w = np.asarray(w, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    return np.transpose(np.matmul(w, x.T), (2, 0, 1))
+
+
+def fold_query_projection(M, wq_nope) -> np.ndarray:
+    """W'_h = M_h @ W_q,nope,h, [H, d_v, d_model] float64. Since q_nope,h =
+    W_q,nope,h x, the absorbed query M_h q_nope,h equals W'_h x."""
+    return np.matmul(np.asarray(M, dtype=np.float64), np.asarray(wq_nope, dtype=np.float64))
+
+
+def gva_layer_decode_step(V, kr_pre, x, wq_nope, wq_rope, M, seq_lens, scale: float,
+                          base: float, cache_dtype: str) -> np.ndarray:
+    """One layer's decode step from the new tokens' hidden states x [B, d_model],
+    by the plain definition: q_nope = W_q,nope x and the pre-RoPE positional
+    slice q_rope = W_q,rope x (float64, never rounded), then gva_decode_step
+    with the materialized keys V_g(h) M_h. A folded path (W' = M W_q,nope,
+    q' = W' x, no M in the decode) must reach the same result."""
+    q_nope = query_projection(x, wq_nope)
+    q_rope = query_projection(x, wq_rope)
+    return gva_decode_step(V, kr_pre, q_nope, q_rope, M, seq_lens, scale, base, cache_dtype)
+
+
 def gqa_decode(q, K, V, seq_lens, scale: float) -> np.ndarray:
     """Plain GQA decode: head h attends to K/V of group h // (H/G).
     q [B, H, d_h]; K, V [B, G, >=n, d_h] (K already rotated)."""

@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import oracle as O
+import workloads as W
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -414,3 +415,73 @@ def test_step_rounds_cached_keys_to_cache_dtype():
     kr_cache = O.round_bf16(O.rope(kr_pre, np.arange(n)))
     ref = O.gva_decode(V, [kr_cache], q_nope, O.rope(q_rope, np.array([[n - 1]])), M, [n], 0.3)
     assert np.array_equal(out, ref)
+
+
+# ---------------------------------------------------------------------------
+# Query projection and the fold of the maps into it ([digest] 与现有产品 /
+# 工作流的接口: the reconstruction matrix can be folded into the query
+# projection at inference)
+# ---------------------------------------------------------------------------
+
+def test_query_projection_matches_per_head_dot_products():
+    """Against scalar loops over heads, channels and the hidden dimension."""
+    rng = np.random.default_rng(40)
+    H, d, d_model, B = 3, 5, 7, 2
+    w = rng.standard_normal((H, d, d_model))
+    x = rng.standard_normal((B, d_model))
+    got = O.query_projection(x, w)
+    for b in range(B):
+        for h in range(H):
+            for i in range(d):
+                ref = sum(float(w[h, i, m]) * float(x[b, m]) for m in range(d_model))
+                assert abs(got[b, h, i] - ref) < 1e-12
+
+
+def test_fold_closed_forms():
+    """Folding the identity map gives the projection back; folding into an
+    identity projection (d_model = d_n) gives the maps back."""
+    rng = np.random.default_rng(41)
+    H, d, d_model = 2, 4, 6
+    wq = rng.standard_normal((H, d, d_model))
+    M = rng.standard_normal((H, d, d))
+    eye = np.broadcast_to(np.eye(d), (H, d, d))
+    assert np.allclose(O.fold_query_projection(eye, wq), wq, rtol=0, atol=0)
+    assert np.allclose(O.fold_query_projection(M, eye), M, rtol=0, atol=0)
+
+
+def test_layer_step_with_selection_projection_is_the_step():
+    """With x holding every head's (q_nope, q_rope) and the projection rows
+    selecting them, the layer step reduces to the step on those queries."""
+    wl = W.Workload("pin_layer", 9, B=2, H=4, G=2, d_n=8, d_v=8, d_r=4, S=9, dtype="f32")
+    inp = W.make_gva_inputs(wl, seed=42)
+    dq = wl.d_n + wl.d_r
+    d_model = wl.H * dq
+    x = np.zeros((wl.B, d_model))
+    wq_nope = np.zeros((wl.H, wl.d_n, d_model))
+    wq_rope = np.zeros((wl.H, wl.d_r, d_model))
+    for h in range(wl.H):
+        x[:, h * dq:h * dq + wl.d_n] = inp.q_nope[:, h]
+        x[:, h * dq + wl.d_n:(h + 1) * dq] = inp.q_rope[:, h]
+        wq_nope[h, :, h * dq:h * dq + wl.d_n] = np.eye(wl.d_n)
+        wq_rope[h, :, h * dq + wl.d_n:(h + 1) * dq] = np.eye(wl.d_r)
+    got = O.gva_layer_decode_step(inp.V, inp.kr, x, wq_nope, wq_rope, inp.M, inp.lens, wl.scale,
+                                  10000.0, "f32")
+    ref = O.gva_decode_step(inp.V, inp.kr, inp.q_nope, inp.q_rope, inp.M, inp.lens, wl.scale,
+                            10000.0, "f32")
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_folded_query_gives_the_materialized_scores():
+    """Absorption through the fold: decoding with q' = (M W_q,nope) x against
+    plain values (identity maps, K = V) equals the layer step with the
+    materialized keys V M and q_nope = W_q,nope x ([digest] 方法, Q' = Q M^T)."""
+    wl = W.Workload("pin_fold", 9, B=2, H=4, G=2, d_n=8, d_v=8, d_r=4, S=11, dtype="f32")
+    inp = W.make_gva_inputs(wl, seed=43)
+    x, wq_nope, wq_rope = W.make_projection_inputs(wl, d_model=16, seed=44)
+    layer = O.gva_layer_decode_step(inp.V, inp.kr, x, wq_nope, wq_rope, inp.M, inp.lens, wl.scale,
+                                    10000.0, "f32")
+    q_abs = O.query_projection(x, O.fold_query_projection(inp.M, wq_nope))
+    eye = np.broadcast_to(np.eye(wl.d_v), (wl.H, wl.d_v, wl.d_v))
+    folded = O.gva_decode_step(inp.V, inp.kr, q_abs, O.query_projection(x, wq_rope), eye, inp.lens,
+                               wl.scale, 10000.0, "f32")
+    assert np.allclose(folded, layer, rtol=1e-11, atol=1e-12)

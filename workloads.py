@@ -155,6 +155,18 @@ def make_gqa_inputs(wl: Workload, seed: Optional[int] = None):
     return q, K, V
 
 
+def make_projection_inputs(wl: Workload, d_model: int, seed: Optional[int] = None):
+    """Hidden states and query-projection weights of one layer: x [B, d_model]
+    ~ N(0, 1); W_q,nope [H, d_n, d_model] and W_q,rope [H, d_r, d_model] ~
+    N(0, 1/d_model), so the projected queries are ~ N(0, 1) like the directly
+    drawn ones. Each rounded once to the workload dtype."""
+    rng = np.random.Generator(np.random.PCG64((wl.seed if seed is None else seed) + 2000))
+    x = round_storage(rng.standard_normal((wl.B, d_model)), wl.dtype)
+    wq_nope = round_storage(rng.standard_normal((wl.H, wl.d_n, d_model)) / math.sqrt(d_model), wl.dtype)
+    wq_rope = round_storage(rng.standard_normal((wl.H, wl.d_r, d_model)) / math.sqrt(d_model), wl.dtype)
+    return x, wq_nope, wq_rope
+
+
 def draw_post_rope(wl: Workload, lens: np.ndarray, rows_extra: int = 0,
                    seed: int = 0):
     """Draw k_r and q_rope directly as post-RoPE values (for decode-only
