@@ -58,7 +58,7 @@ def parse():
     p.add_argument("--profile-copy-mb", type=int, default=0,
                    help="with --profile-step/--profile-decode: first run a plain elementwise copy "
                         "(read N MiB, write N MiB) three times, the reference for traffic counters")
-    p.add_argument("--mode", choices=["step", "gqa", "folded"], default="step")
+    p.add_argument("--mode", choices=["step", "gqa", "folded", "multi"], default="step")
     return p.parse_args()
 
 
@@ -87,6 +87,9 @@ def main():
         return
     if args.mode == "folded":
         folded_compare(args)
+        return
+    if args.mode == "multi":
+        multi_compare(args)
         return
     wl = W.WORKLOADS[args.workload]
     if args.split >= 0:
@@ -476,6 +479,67 @@ def folded_compare(args):
                               "folded": round(1e6 / res["folded_layer_step_us"], 1)},
         "projection_weight_bytes": wl.H * (wl.d_v + wl.d_r) * d_model * 2,
     })
+    print(json.dumps(res), flush=True)
+
+
+def multi_compare(args):
+    """`--mode multi`: gva_decode_multi with n_q = 1, 2, 4 queries per sequence
+    (the last n_q tokens, causal among them) on the mid shape, K launches in a
+    graph over cold replicas. The cache bytes per launch are the same; the
+    query tokens served per launch grow with n_q."""
+    import numpy as np
+    import torch
+
+    import compact_kv_cache_amd as gva
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS[args.workload]
+    K = args.steps
+    n = wl.S + 4
+    bpt = gva.gva_cache_bytes_per_token(wl.G, wl.d_v, wl.d_r, wl.dtype)
+    nbytes = wl.B * n * bpt
+    R = max(2, math.ceil(512e6 / nbytes))
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 5))
+    V0 = torch.from_numpy(rng.standard_normal((wl.B, wl.G, n, wl.d_v), dtype=np.float32)).to(dev).bfloat16()
+    K0 = torch.from_numpy(rng.standard_normal((wl.B, n, wl.d_r), dtype=np.float32)).to(dev).bfloat16()
+    reps = [(V0.clone(), K0.clone(), (torch.randn(wl.H, wl.d_v, wl.d_n, device=dev) / 8).bfloat16())
+            for _ in range(R)]
+    del V0, K0
+    seq = torch.full((wl.B,), n, dtype=torch.int32, device=dev)
+    shape = gva.make_shape(wl.B, wl.H, wl.G, wl.d_n, wl.d_v, wl.d_r, capacity=n, max_seq_len=n, dtype=wl.dtype)
+    res = {"mode": "multi_compare",
+           "config": {"workload": f"{wl.name}: B={wl.B} n={n} H={wl.H} G={wl.G} d_v=d_n={wl.d_v} d_r={wl.d_r} "
+                                  f"{wl.dtype}, contiguous, {R} cold replicas", "steps": K},
+           "cache_bytes_per_launch": nbytes}
+    for nq in (1, 2, 4):
+        q = torch.randn(wl.B, nq, wl.H, wl.d_n, device=dev).bfloat16()
+        qr = torch.randn(wl.B, nq, wl.H, wl.d_r, device=dev).bfloat16()
+        out = torch.empty(wl.B, nq, wl.H, wl.d_v, dtype=torch.bfloat16, device=dev)
+        ws = torch.zeros(max(gva.gva_decode_multi_workspace_bytes(shape, nq), 4) // 4 + 1,
+                         dtype=torch.float32, device=dev)
+
+        def call(i):
+            v, k, M = reps[i % R]
+            gva.gva_decode_multi(shape, nq, q, qr, M, v, k, seq, None, wl.scale, out, ws)
+
+        for i in range(2 * R):
+            call(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                call(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / K * 1e3
+        res[f"nq{nq}"] = {"us": round(us, 3), "cache_GBps": round(nbytes / us / 1e3, 1),
+                          "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4),
+                          "query_tokens_per_s": round(wl.B * nq / us * 1e6, 1)}
     print(json.dumps(res), flush=True)
 
 

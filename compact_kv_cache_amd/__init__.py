@@ -17,7 +17,8 @@ from ._lib import GVA_BF16, GVA_F32, GvaShape
 __all__ = [
     "GvaShape", "GVA_F32", "GVA_BF16", "GvaError", "make_shape", "lib",
     "gva_append", "gva_rope_query", "gva_decode", "gva_decode_step", "gva_gqa_ref_decode",
-    "gva_fold_query_projection", "gva_query_projection",
+    "gva_fold_query_projection", "gva_query_projection", "gva_rope_query_multi", "gva_decode_multi",
+    "gva_decode_multi_workspace_bytes",
     "gva_decode_workspace_bytes", "gva_decode_step_workspace_bytes", "gva_decode_split_tokens", "gva_cache_bytes_per_token",
     "gva_status_string", "gva_abi_version", "workspace_for",
 ]
@@ -112,6 +113,31 @@ def gva_decode_step(shape: GvaShape, v_new, kr_new, q_nope, q_rope, M, v_cache, 
                                float(rope_base), _ptr(out, dt, "out"),
                                _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream)),
            "gva_decode_step")
+
+
+def gva_rope_query_multi(shape: GvaShape, n_q: int, q_rope_in, q_rope_out, seq_lens,
+                         rope_base: float = 10000.0, stream=None) -> None:
+    dt = _TORCH.get(shape.dtype)
+    _check(lib.gva_rope_query_multi(shape, int(n_q), _ptr(q_rope_in, dt, "q_rope_in"),
+                                    _ptr(q_rope_out, dt, "q_rope_out"),
+                                    _ptr(seq_lens, torch.int32, "seq_lens"), float(rope_base),
+                                    _stream(stream)), "gva_rope_query_multi")
+
+
+def gva_decode_multi(shape: GvaShape, n_q: int, q_nope, q_rope, M, v_cache, kr_cache, seq_lens,
+                     block_table, scale: float, out, workspace=None, stream=None) -> None:
+    dt = _TORCH.get(shape.dtype)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gva_decode_multi(shape, int(n_q), _ptr(q_nope, dt, "q_nope"), _ptr(q_rope, dt, "q_rope"),
+                                _ptr(M, dt, "M"), _ptr(v_cache, dt, "v_cache"),
+                                _ptr(kr_cache, dt, "kr_cache"), _ptr(seq_lens, torch.int32, "seq_lens"),
+                                _ptr(block_table, torch.int32, "block_table"), float(scale),
+                                _ptr(out, dt, "out"), _ptr(workspace, None, "workspace"), ws_bytes,
+                                _stream(stream)), "gva_decode_multi")
+
+
+def gva_decode_multi_workspace_bytes(shape: GvaShape, n_q: int) -> int:
+    return int(lib.gva_decode_multi_workspace_bytes(shape, int(n_q)))
 
 
 def gva_fold_query_projection(M, wq_nope, w_fold, stream=None) -> None:

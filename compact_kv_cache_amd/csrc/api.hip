@@ -93,9 +93,9 @@ int n_splits(const gva_shape* s, int split) {
   return s->max_seq_len <= 0 ? 1 : (s->max_seq_len + split - 1) / split;
 }
 
-size_t workspace_for(const gva_shape* s) {
+size_t workspace_for(const gva_shape* s, int nq = 1) {
   const int split = resolve_split(s);
-  return gva::ws_total_bytes(s->B, s->H, s->G, n_splits(s, split));
+  return gva::ws_total_bytes(s->B, s->H, s->G, n_splits(s, split), nq);
 }
 
 void set_workspace(gva::DecodeLaunch& a, void* workspace) {
@@ -104,7 +104,7 @@ void set_workspace(gva::DecodeLaunch& a, void* workspace) {
   a.counters = reinterpret_cast<int32_t*>(base);
   a.counters_seq = a.counters + (size_t)a.B * a.G;
   a.ws_o = reinterpret_cast<float*>(base + gva::ws_counter_bytes(a.B, a.G));
-  a.ws_ml = a.ws_o + (size_t)a.B * a.H * a.n_split * 64;
+  a.ws_ml = a.ws_o + (size_t)a.B * a.nq * a.H * a.n_split * 64;
 }
 
 size_t step_workspace_for(const gva_shape* s) {
@@ -136,6 +136,7 @@ gva::DecodeLaunch make_decode(const gva_shape* s) {
   a.n_split = n_splits(s, a.split);
   a.paged = s->block_size != 0;
   a.bf16 = s->dtype == GVA_BF16;
+  a.nq = 1;
   return a;
 }
 
@@ -178,8 +179,15 @@ gva_status gva_append(const gva_shape* shape, const void* v_new, const void* kr_
 
 gva_status gva_rope_query(const gva_shape* shape, const void* q_rope_in, void* q_rope_out,
                           const int32_t* seq_lens, float rope_base, hipStream_t stream) {
+  return gva_rope_query_multi(shape, 1, q_rope_in, q_rope_out, seq_lens, rope_base, stream);
+}
+
+gva_status gva_rope_query_multi(const gva_shape* shape, int32_t n_q, const void* q_rope_in, void* q_rope_out,
+                                const int32_t* seq_lens, float rope_base, hipStream_t stream) {
   gva_status st = check_shape(shape, false);
   if (st != GVA_OK) return st;
+  if (n_q < 1 || (int64_t)n_q * shape->B * shape->H * shape->d_r > INT32_MAX)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "n_q = %d must be >= 1", n_q);
   if (shape->d_r == 0) return ok();
   if (!q_rope_in || !q_rope_out || !seq_lens)
     return fail(GVA_ERR_INVALID_ARGUMENT, "q_rope_in, q_rope_out and seq_lens must be non-NULL");
@@ -188,6 +196,7 @@ gva_status gva_rope_query(const gva_shape* shape, const void* q_rope_in, void* q
   a.B = shape->B;
   a.H = shape->H;
   a.d_r = shape->d_r;
+  a.nq = n_q;
   a.bf16 = shape->dtype == GVA_BF16;
   a.q_in = q_rope_in;
   a.q_out = q_rope_out;
@@ -200,8 +209,20 @@ gva_status gva_decode(const gva_shape* shape, const void* q_nope, const void* q_
                       const void* v_cache, const void* kr_cache, const int32_t* seq_lens,
                       const int32_t* block_table, float scale, void* out, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
+  return gva_decode_multi(shape, 1, q_nope, q_rope, M, v_cache, kr_cache, seq_lens, block_table, scale, out,
+                          workspace, workspace_bytes, stream);
+}
+
+gva_status gva_decode_multi(const gva_shape* shape, int32_t n_q, const void* q_nope, const void* q_rope,
+                            const void* M, const void* v_cache, const void* kr_cache, const int32_t* seq_lens,
+                            const int32_t* block_table, float scale, void* out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
   gva_status st = check_shape(shape, false);
   if (st != GVA_OK) return st;
+  if (n_q != 1 && n_q != 2 && n_q != 4)
+    return fail(GVA_ERR_UNSUPPORTED, "n_q = %d; built for 1, 2 or 4 queries per sequence", n_q);
+  if (n_q > 1 && (shape->dtype != GVA_BF16 || force_valu()))
+    return fail(GVA_ERR_UNSUPPORTED, "several queries per sequence need the bf16 matrix-core kernel");
   if (!q_nope || !v_cache || !seq_lens || !out)
     return fail(GVA_ERR_INVALID_ARGUMENT, "q_nope, v_cache, seq_lens and out must be non-NULL");
   if (shape->d_r > 0 && (!q_rope || !kr_cache))
@@ -210,11 +231,12 @@ gva_status gva_decode(const gva_shape* shape, const void* q_nope, const void* q_
     return fail(GVA_ERR_INVALID_ARGUMENT, "paged cache needs a block_table");
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(GVA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0 (got %g)", (double)scale);
-  const size_t need = workspace_for(shape);
+  const size_t need = workspace_for(shape, n_q);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
   gva::DecodeLaunch a = make_decode(shape);
+  a.nq = n_q;
   a.q_nope = q_nope;
   a.q_rope = q_rope;
   a.M = M;
@@ -302,6 +324,7 @@ gva_status gva_decode_step(const gva_shape* shape, const void* v_new, const void
     rq.B = shape->B;
     rq.H = shape->H;
     rq.d_r = shape->d_r;
+    rq.nq = 1;
     rq.bf16 = ap.bf16;
     rq.q_in = q_rope;
     rq.q_out = q_rot;
@@ -357,6 +380,11 @@ gva_status gva_query_projection(const gva_shape* shape, int32_t d_model, const v
   gva::ProjectLaunch a{shape->B, shape->H, shape->d_v, shape->d_r, d_model, shape->dtype == GVA_BF16,
                        x, w_fold, w_rope, q_abs, q_rope};
   return hip_status(gva::launch_project(a, stream), "gva_query_projection launch");
+}
+
+size_t gva_decode_multi_workspace_bytes(const gva_shape* shape, int32_t n_q) {
+  if (check_shape(shape, false) != GVA_OK || n_q < 1) return 0;
+  return workspace_for(shape, n_q);
 }
 
 size_t gva_decode_step_workspace_bytes(const gva_shape* shape) {

@@ -65,16 +65,19 @@ __global__ void advance_kernel(int32_t* seq_lens, int B, int n_new, int cap_toke
   if (b < B) seq_lens[b] = min(max(seq_lens[b], 0) + n_new, cap_tokens);
 }
 
+// q[b][j] (j < nq) is the query of the token at position seq_lens[b] - nq + j
+// (the last nq cached tokens; nq = 1: the newest one).
 template <typename T>
 __global__ __launch_bounds__(256) void rope_query_kernel(RopeQueryLaunch a) {
   const int b = blockIdx.x;
   const int half = a.d_r / 2;
-  const double pos = (double)max(a.seq_lens[b] - 1, 0);
+  const int len = a.seq_lens[b];
   const T* src = reinterpret_cast<const T*>(a.q_in);
   T* dst = reinterpret_cast<T*>(a.q_out);
-  for (int i = threadIdx.x; i < a.H * half; i += blockDim.x) {
-    const int h = i / half, p = i % half;
-    const int64_t off = ((int64_t)b * a.H + h) * a.d_r + 2 * p;
+  for (int i = threadIdx.x; i < a.nq * a.H * half; i += blockDim.x) {
+    const int j = i / (a.H * half), h = (i / half) % a.H, p = i % half;
+    const double pos = (double)max(len - a.nq + j, 0);
+    const int64_t off = (((int64_t)b * a.nq + j) * a.H + h) * a.d_r + 2 * p;
     T y0, y1;  // (the rotation may be in place)
     rope_store<T>(to_f32(src[off]), to_f32(src[off + 1]), pos, a.rope.theta[p], y0, y1);
     dst[off] = y0;

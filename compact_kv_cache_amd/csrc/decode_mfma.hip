@@ -114,9 +114,15 @@ struct Frags {
 // position of 16 consecutive rows then touches 16 distinct bank groups.
 __device__ __forceinline__ int stage_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <int HPG, bool PAGED, int KR, bool GQA, bool STEP>
+template <int HPG, bool PAGED, int KR, bool GQA, bool STEP, int NQ>
 __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunch a) {
   constexpr bool DR = KR > 0;  // positional slice present (d_r = 8 * KR)
+  // NQ queries per sequence (the last NQ cached tokens, each reading the cache
+  // up to its own position); the matrix-core column col carries query
+  // (col % NCOL) / HPG of head (col % NCOL) % HPG.
+  constexpr int NCOL = NQ * HPG;
+  static_assert(NCOL <= 16, "at most 16 (query, head) columns");
+  static_assert(NQ == 1 || (!GQA && !STEP), "several queries: GVA decode only");
   static_assert(!(GQA && DR), "GQA reference has no positional slice");
   static_assert(!(GQA && STEP), "the fused step is GVA only");
   const int tid = threadIdx.x, lane = tid & 63;
@@ -140,12 +146,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   const int t_end_max = min(a.max_seq_len, t_begin + a.split);
   const int tiles_max = max(t_end_max - t_begin + kTile - 1, 0) / kTile;
   const float sl2 = a.scale * kLog2e;
-  const int jcol = col % HPG;        // head (within the group) of this lane's column
+  const int ccol = col % NCOL;
+  const int jcol = ccol % HPG;       // head (within the group) of this lane's column
+  const int jq = ccol / HPG;         // query of this lane's column
   const int h_col = g * HPG + jcol;  // its global head index
 
-  __shared__ float qsh[4][kD];            // [head][channel] absorbed queries
-  __shared__ float red_o[kWaves][4][kD];  // per-wave unnormalized outputs
-  __shared__ float red_ml[kWaves][4][2];  // per-wave (max in log2 units, sum)
+  __shared__ float qsh[NQ][4][kD];           // [query][head][channel] absorbed queries
+  __shared__ float red_o[kWaves][NCOL][kD];  // per-wave unnormalized outputs
+  __shared__ float red_ml[kWaves][NCOL][2];  // per-wave (max in log2 units, sum)
   __shared__ __bf16 qrot_sh[4][32];       // fused step: rotated query slices
   __shared__ __attribute__((aligned(16))) __bf16 krot_sh[32];  // fused step: rotated appended key
   __shared__ __attribute__((aligned(16))) __bf16 vnew_sh[kD];  // fused step: appended value row
@@ -163,7 +171,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   const int gm_j = (w & 3) % HPG, gm_half = w >> 2;
   const int h_w = g * HPG + gm_j;
   Frag mA[2][2], qB[2];
-  uint32_t qv_bits = 0;  // folded or GQA query element (bf16 bits), converted after the tile issue
+  uint32_t qv_bits[NQ];  // folded or GQA query elements (bf16 bits), converted after the tile issue
   // M == nullptr: the query projection already carries the reconstruction
   // map (GVA digest, section 与现有产品 / 工作流的接口: the map can be folded
   // into the query projection), so q_nope holds q' = M_h q_nope,h itself and
@@ -179,13 +187,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       for (int kc2 = 0; kc2 < 2; ++kc2) mA[m][kc2].u = ld16(Mh, chan * kD + 32 * kc2 + 8 * r);
     }
 #pragma unroll
-    for (int kc2 = 0; kc2 < 2; ++kc2) qB[kc2].u = ld16(qn + ((int64_t)b * H + h_w) * kD, 32 * kc2 + 8 * r);
+    for (int kc2 = 0; kc2 < 2; ++kc2)
+      qB[kc2].u = ld16(qn + (((int64_t)b * NQ + col % NQ) * H + h_w) * kD, 32 * kc2 + 8 * r);  // column = query
   }
   // (loaded in every mode, so that no wave waits for it inside a branch)
-  qv_bits = reinterpret_cast<const uint16_t*>(qn)[((int64_t)b * H + h_w) * kD + lane];
+#pragma unroll
+  for (int jj = 0; jj < NQ; ++jj)
+    qv_bits[jj] = reinterpret_cast<const uint16_t*>(qn)[(((int64_t)b * NQ + jj) * H + h_w) * kD + lane];
   Frag qr;
   if constexpr (DR && !STEP)
-    qr.u = ld16(reinterpret_cast<const __bf16*>(a.q_rope) + ((int64_t)b * H + h_col) * d_r, kr_off);
+    qr.u = ld16(reinterpret_cast<const __bf16*>(a.q_rope) + (((int64_t)b * NQ + jq) * H + h_col) * d_r, kr_off);
   // Fused step: the appended value row (lane l holds channels 8*(l%8) .. +7);
   // it is kept in LDS, not in registers, for the one tile that holds it.
   u32x4 vnew_l = u32x4{0u, 0u, 0u, 0u};
@@ -313,6 +324,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   }
   const int t_end = min(n, t_begin + a.split);
   const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;  // 0 only when n == 0
+  const int p_col = n - NQ + jq;       // last token this lane's query reads (several queries)
+  const int causal_lo = n - NQ + 1;    // tokens before it are read by every query
 
   // Registers -> LDS stage (plain contiguous stores), then the operand
   // fragments back. LDS operations of one wave complete in order, so the
@@ -383,13 +396,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       D[m] = mma(mA[m][0], qB[0], kZero4);
       D[m] = mma(mA[m][1], qB[1], D[m]);
     }
-    // lane (col 0, group r) holds q'[32 * half + 8r + e] in D[e / 4][e % 4]
-    if (col == 0) {
+    // lane (col = query < NQ, group r) holds q'[32 * half + 8r + e] in D[e / 4][e % 4]
+    if (col < NQ) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qsh[gm_j][32 * gm_half + 8 * r + e] = D[e >> 2][e & 3];
+      for (int e = 0; e < 8; ++e) qsh[col][gm_j][32 * gm_half + 8 * r + e] = D[e >> 2][e & 3];
     }
   } else {
-    if (gm_half == 0) qsh[gm_j][lane] = __uint_as_float(qv_bits << 16);
+    if (gm_half == 0) {
+#pragma unroll
+      for (int jj = 0; jj < NQ; ++jj) qsh[jj][gm_j][lane] = __uint_as_float(qv_bits[jj] << 16);
+    }
   }
   if constexpr (STEP) {
     if (w == 0 && lane < 8) *reinterpret_cast<u32x4*>(vnew_sh + 8 * lane) = vnew_l;
@@ -414,7 +430,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
 #pragma unroll
   for (int kc2 = 0; kc2 < 2; ++kc2) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qb[kc2].h[e] = (__bf16)qsh[jcol][32 * kc2 + 8 * r + e];
+    for (int e = 0; e < 8; ++e) qb[kc2].h[e] = (__bf16)qsh[jq][jcol][32 * kc2 + 8 * r + e];
   }
   if constexpr (STEP && DR) {
 #pragma unroll
@@ -496,12 +512,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       if constexpr (DR) c = mma(T.kr[st], qr, c);
       s[st] = c;
     }
-    if (!T.full) {
+    // Masks: tokens past the partition end, and (several queries) tokens past
+    // the column's own position; tokens below causal_lo are seen by all.
+    if (!T.full || (NQ > 1 && T.t0 + kTile > causal_lo)) {
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (T.t0 + 16 * st + 4 * r + i >= t_end) s[st][i] = -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          const int tok = T.t0 + 16 * st + 4 * r + i;
+          if (tok >= t_end || (NQ > 1 && tok > p_col)) s[st][i] = -INFINITY;
+        }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -512,13 +532,15 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = (mx > m_ref + thr) ? mx : m_ref;
     if (__any(m_new != m_ref)) {
-      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * sl2);  // 0 on the first tile
+      // 0 on a column's first tile; 1 where the max does not move (also a
+      // column that has seen only masked scores so far)
+      const float alpha = (m_new == m_ref) ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * sl2);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db) acc_o[db] *= alpha;
       m_ref = m_new;
     }
-    const float bias = -m_ref * sl2;
+    const float bias = (m_ref == -INFINITY) ? 0.f : -m_ref * sl2;  // all-masked column: p = 0
     float psum = 0.f;
 #pragma unroll
     for (int st = 0; st < 4; ++st)
@@ -581,7 +603,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   // ---- merge the waves ----------------------------------------------------------------
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  if (col < HPG) {
+  if (col < NCOL) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -592,54 +614,82 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     }
   }
   __syncthreads();
-  const int j = tid >> 6, d = lane;  // merge thread: head j (< HPG) of the group, channel d
-  float o = 0.f, l = 0.f, mfin = -INFINITY;
-  if (j < HPG) {
+  // merge thread: column jj = wave + 8u (query jj / HPG, head jj % HPG), channel d
+  constexpr int kPer = (NCOL + kWaves - 1) / kWaves;
+  const int d = lane;
+  float o[kPer], l[kPer], mfin[kPer];
+  int64_t orow[kPer];  // (sequence, query, head) row of the output and of the partials
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) mfin = fmaxf(mfin, red_ml[ww][j][0]);
-    if (mfin > -INFINITY) {
+  for (int u = 0; u < kPer; ++u) {
+    const int jj = (tid >> 6) + u * kWaves;
+    o[u] = 0.f;
+    l[u] = 0.f;
+    mfin[u] = -INFINITY;
+    orow[u] = ((int64_t)b * NQ + jj / HPG) * H + g * HPG + jj % HPG;
+    if (jj < NCOL) {
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        const float f = exp2f(red_ml[ww][j][0] - mfin);
-        o = fmaf(f, red_o[ww][j][d], o);
-        l = fmaf(f, red_ml[ww][j][1], l);
+      for (int ww = 0; ww < kWaves; ++ww) mfin[u] = fmaxf(mfin[u], red_ml[ww][jj][0]);
+      if (mfin[u] > -INFINITY) {
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float f = exp2f(red_ml[ww][jj][0] - mfin[u]);
+          o[u] = fmaf(f, red_o[ww][jj][d], o[u]);
+          l[u] = fmaf(f, red_ml[ww][jj][1], l[u]);
+        }
       }
     }
   }
   __bf16* out = reinterpret_cast<__bf16*>(a.out);
-  const int h = g * HPG + j;
   if (n_parts <= 1) {
-    if (j < HPG) out[((int64_t)b * H + h) * kD + d] = (__bf16)(l > 0.f ? o / l : 0.f);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if ((tid >> 6) + u * kWaves < NCOL) out[orow[u] * kD + d] = (__bf16)(l[u] > 0.f ? o[u] / l[u] : 0.f);
     finish_step();
     return;
   }
-  const int64_t slot0 = ((int64_t)b * H + h) * a.n_split;
-  if (j < HPG) {
-    st_dev(a.ws_o + (slot0 + split) * kD + d, o);
-    if (d == 0) {
-      st_dev(a.ws_ml + 2 * (slot0 + split), mfin);
-      st_dev(a.ws_ml + 2 * (slot0 + split) + 1, l);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    if ((tid >> 6) + u * kWaves < NCOL) {
+      const int64_t slot = orow[u] * a.n_split + split;
+      st_dev(a.ws_o + slot * kD + d, o[u]);
+      if (d == 0) {
+        st_dev(a.ws_ml + 2 * slot, mfin[u]);
+        st_dev(a.ws_ml + 2 * slot + 1, l[u]);
+      }
     }
   }
   int32_t* counter = a.counters + (int64_t)b * G + g;
   if (arrive_last(counter, n_parts)) {
-    if (j < HPG)
-      out[((int64_t)b * H + h) * kD + d] = (__bf16)merge_partials(a.ws_o, a.ws_ml, slot0, n_parts, d);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if ((tid >> 6) + u * kWaves < NCOL)
+        out[orow[u] * kD + d] = (__bf16)merge_partials(a.ws_o, a.ws_ml, orow[u] * a.n_split, n_parts, d);
     if (tid == 0) reset_counter(counter);
   }
   finish_step();
 }
 
-template <int HPG, int KR, bool GQA, bool STEP>
-hipError_t mfma_paged(const DecodeLaunch& a, hipStream_t s) {
+template <int HPG, int KR, bool GQA, bool STEP, int NQ>
+hipError_t mfma_launch(const DecodeLaunch& a, hipStream_t s) {
   const int pairs = a.B * a.n_split;
   const dim3 grid(((pairs + 7) / 8) * 8 * a.G);
   if (a.paged)
-    decode_mfma_kernel<HPG, true, KR, GQA, STEP><<<grid, 64 * kWaves, 0, s>>>(a);
+    decode_mfma_kernel<HPG, true, KR, GQA, STEP, NQ><<<grid, 64 * kWaves, 0, s>>>(a);
   else
-    decode_mfma_kernel<HPG, false, KR, GQA, STEP><<<grid, 64 * kWaves, 0, s>>>(a);
+    decode_mfma_kernel<HPG, false, KR, GQA, STEP, NQ><<<grid, 64 * kWaves, 0, s>>>(a);
   return hipGetLastError();
 }
+
+// queries per sequence: 1 (every path), 2 or 4 (GVA decode of several new tokens)
+template <int HPG, int KR, bool GQA, bool STEP>
+hipError_t mfma_paged(const DecodeLaunch& a, hipStream_t s) {
+  if constexpr (!GQA && !STEP) {
+    if (a.nq == 2) return mfma_launch<HPG, KR, false, false, 2>(a, s);
+    if (a.nq == 4) return mfma_launch<HPG, KR, false, false, 4>(a, s);
+  }
+  return mfma_launch<HPG, KR, GQA, STEP, 1>(a, s);
+}
+
 
 // d_r = 8 * KR (validated on the host: 0, 8, 16, 24 or 32)
 template <int HPG, bool GQA, bool STEP>

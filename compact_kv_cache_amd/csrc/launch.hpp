@@ -49,6 +49,7 @@ struct AppendLaunch {
 
 struct RopeQueryLaunch {
   int B, H, d_r;
+  int nq;  // queries per sequence: q[b][j] sits at position seq_lens[b] - nq + j
   bool bf16;
   const void* q_in;
   void* q_out;
@@ -60,6 +61,7 @@ struct RopeQueryLaunch {
 struct DecodeLaunch {
   int B, H, G, d_r, capacity, max_seq_len, num_blocks, max_blocks;
   int split, n_split;  // split-K partition length and count
+  int nq;              // queries per sequence (the last nq tokens; 1, 2 or 4)
   bool paged, bf16;
   const void* q_nope;  // GQA: q
   const void* q_rope;  // rotated; fused step: before RoPE
@@ -72,7 +74,7 @@ struct DecodeLaunch {
   void* out;
   // Workspace: int32 arrival counters (zero before the first call, left zero
   // by every call) -- [B*G] split-K, then [B] fused-step -- then float
-  // partials o [B*H*n_split*64] and (m, l) [B*H*n_split*2].
+  // partials o [B*nq*H*n_split*64] and (m, l) [B*nq*H*n_split*2].
   int32_t* counters;
   int32_t* counters_seq;
   float* ws_o;
@@ -96,9 +98,9 @@ inline size_t ws_partial_bytes(int B, int H, int n_split) {
   return n_split <= 1 ? 0 : (size_t)B * H * n_split * (64 + 2) * sizeof(float);
 }
 inline size_t ws_qrot_bytes(int B, int H) { return (((size_t)B * H * 32 * 4) + 255) / 256 * 256; }
-inline size_t ws_total_bytes(int B, int H, int G, int n_split) {
+inline size_t ws_total_bytes(int B, int H, int G, int n_split, int nq = 1) {
   if (n_split <= 1) return 0;
-  return ws_counter_bytes(B, G) + ws_partial_bytes(B, H, n_split);
+  return ws_counter_bytes(B, G) + ws_partial_bytes(B * nq, H, n_split);
 }
 inline size_t ws_step_bytes(int B, int H, int G, int n_split) {
   return ws_counter_bytes(B, G) + ws_partial_bytes(B, H, n_split) + ws_qrot_bytes(B, H);

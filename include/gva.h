@@ -136,6 +136,17 @@ gva_status gva_rope_query(const gva_shape* shape, const void* q_rope_in, void* q
                           const int32_t* seq_lens, float rope_base, hipStream_t stream);
 
 /*
+ * gva_rope_query_multi - as gva_rope_query for the queries of the last n_q
+ * cached tokens of every sequence (speculative verification, chunked decode):
+ * q[b][j] (j < n_q) belongs to the token at position seq_lens[b] - n_q + j and
+ * is rotated by that position (by 0 where it would be negative).
+ *   q_rope_in, q_rope_out  [B][n_q][H][d_r]  (may alias)
+ * gva_rope_query is the case n_q = 1.
+ */
+gva_status gva_rope_query_multi(const gva_shape* shape, int32_t n_q, const void* q_rope_in, void* q_rope_out,
+                                const int32_t* seq_lens, float rope_base, hipStream_t stream);
+
+/*
  * gva_decode - one decode step of GVA attention over the compact cache.
  * Computes, for every sequence b and head h with n = seq_lens[b] tokens,
  *   s_t   = scale * ( (M_h q_nope[b,h]) . V[b, g(h), t] + q_rope[b,h] . k_r[b, t] )
@@ -172,6 +183,34 @@ gva_status gva_decode(const gva_shape* shape, const void* q_nope, const void* q_
                       const void* M, const void* v_cache, const void* kr_cache,
                       const int32_t* seq_lens, const int32_t* block_table, float scale,
                       void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gva_decode_multi - decode the queries of the last n_q cached tokens of every
+ * sequence at once, each reading the cache up to and including its own token
+ * (a causal mask over the new tokens; [gqa] section on cache growth: a token's
+ * query reads the earlier tokens and itself; the same page's list of cache
+ * lifecycles names speculative decoding). With n = seq_lens[b], query j sits
+ * at position n - n_q + j and attends to tokens t <= n - n_q + j (none, and a
+ * zero output row, where that is negative). The n_q tokens must already be
+ * in the cache (gva_append with n_new = n_q).
+ *   n_q      1, 2 or 4 (2 and 4: bf16 only)
+ *   q_nope   [B][n_q][H][d_n] (or absorbed [B][n_q][H][d_v] when M is NULL)
+ *   q_rope   [B][n_q][H][d_r] rotated (gva_rope_query_multi)
+ *   out      [B][n_q][H][d_v]
+ *   workspace at least gva_decode_multi_workspace_bytes(shape, n_q) bytes,
+ *            same rules as for gva_decode.
+ * Other arguments as for gva_decode, which is the case n_q = 1. The group's
+ * heads times the n_q queries fill the matrix-core columns, so every cache row
+ * read serves n_q * H/G query rows.
+ */
+gva_status gva_decode_multi(const gva_shape* shape, int32_t n_q, const void* q_nope, const void* q_rope,
+                            const void* M, const void* v_cache, const void* kr_cache, const int32_t* seq_lens,
+                            const int32_t* block_table, float scale, void* out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace gva_decode_multi needs for `shape` and n_q (0 when
+ * no sequence is split). Returns 0 for an invalid shape. */
+size_t gva_decode_multi_workspace_bytes(const gva_shape* shape, int32_t n_q);
 
 /*
  * gva_decode_step - one whole decode step in a single call: append one token

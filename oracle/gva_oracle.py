@@ -233,6 +233,38 @@ def gva_decode_step(V, kr_pre, q_nope, q_rope_pre, M, seq_lens, scale: float,
     return gva_decode(V, kr_rot, q_nope, q_rot, M, seq_lens, scale)
 
 
+def gva_decode_multi(V, kr, q_nope, q_rope, M, seq_lens, scale: float) -> np.ndarray:
+    """Decode of the last n_q cached tokens' queries at once. q_nope
+    [B, n_q, H, d_n], q_rope [B, n_q, H, d_r] (rotated). Query j of sequence b
+    sits at position p = n - n_q + j (n = seq_lens[b]) and reads the tokens up
+    to and including its own, t <= p ([gqa] KV Cache 为什么会不断变大); a
+    negative p reads nothing (zero row). Returns [B, n_q, H, d_v] float64."""
+    q_nope = np.asarray(q_nope)
+    B, nq = q_nope.shape[:2]
+    out = np.zeros((B, nq, q_nope.shape[2], V[0].shape[-1]))
+    for b in range(B):
+        n = int(seq_lens[b])
+        for j in range(nq):
+            p = n - nq + j
+            if p >= 0:
+                out[b, j] = gva_decode_seq(V[b], kr[b], q_nope[b, j], q_rope[b, j], M, p + 1, scale)
+    return out
+
+
+def gva_decode_multi_step(V, kr_pre, q_nope, q_rope_pre, M, seq_lens, scale: float,
+                          base: float, cache_dtype: str) -> np.ndarray:
+    """As gva_decode_multi from pre-RoPE inputs: the cache holds RoPE_t(k~_r[t])
+    rounded to the cache dtype, query j is rotated at its own position
+    n - n_q + j (float64)."""
+    q_rope_pre = np.asarray(q_rope_pre, dtype=np.float64)
+    nq = q_rope_pre.shape[1]
+    kr_rot = [append_positional_keys(np.asarray(k)[:int(n)], 0, base, cache_dtype)
+              for k, n in zip(kr_pre, seq_lens)]
+    pos = np.maximum(np.asarray(seq_lens, dtype=np.float64)[:, None] - nq + np.arange(nq)[None, :], 0.0)
+    q_rot = rope(q_rope_pre, pos[:, :, None], base)
+    return gva_decode_multi(V, kr_rot, q_nope, q_rot, M, seq_lens, scale)
+
+
 # ---------------------------------------------------------------------------
 # The query projection, and the maps folded into it ([digest] 与现有产品 /
 # 工作流的接口: at inference the reconstruction matrix can be folded into the

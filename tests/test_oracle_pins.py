@@ -485,3 +485,54 @@ def test_folded_query_gives_the_materialized_scores():
     folded = O.gva_decode_step(inp.V, inp.kr, q_abs, O.query_projection(x, wq_rope), eye, inp.lens,
                                wl.scale, 10000.0, "f32")
     assert np.allclose(folded, layer, rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Several new tokens' queries at once (causal over the new tokens)
+# ---------------------------------------------------------------------------
+
+def test_multi_query_decode_brute_force_causal_mask():
+    """Scalar loops with an explicit causal mask over the whole cache: query j
+    at position n - n_q + j sees token t only when t <= n - n_q + j."""
+    wl = W.Workload("pin_multi", 9, B=2, H=4, G=2, d_n=4, d_v=4, d_r=2, S=0, dtype="f32")
+    lens = np.array([5, 3])
+    inp = W.make_gva_inputs(wl, lens=lens, seed=50)
+    nq = 4
+    rng = np.random.default_rng(51)
+    qn = rng.standard_normal((2, nq, 4, 4))
+    qr = rng.standard_normal((2, nq, 4, 2))
+    got = O.gva_decode_multi(inp.V, inp.kr, qn, qr, inp.M, lens, 0.4)
+    for b in range(2):
+        n = int(lens[b])
+        for j in range(nq):
+            p = n - nq + j
+            for h in range(4):
+                g = h // 2
+                s = []
+                for t in range(n):
+                    if t > p:
+                        s.append(-math.inf)
+                        continue
+                    k_c = [sum(inp.V[b][g, t, v] * inp.M[h][v, c] for v in range(4)) for c in range(4)]
+                    dot = sum(k_c[c] * qn[b, j, h, c] for c in range(4))
+                    dot += sum(inp.kr[b][t, c] * qr[b, j, h, c] for c in range(2))
+                    s.append(0.4 * dot)
+                mx = max(s)
+                if mx == -math.inf:
+                    assert np.all(got[b, j, h] == 0.0)
+                    continue
+                w = [math.exp(x - mx) for x in s]
+                tot = sum(w)
+                for c in range(4):
+                    ref = sum(w[t] * inp.V[b][g, t, c] for t in range(n)) / tot
+                    assert abs(got[b, j, h, c] - ref) < 1e-12
+
+
+def test_multi_query_single_is_decode():
+    wl = W.Workload("pin_multi1", 9, B=3, H=8, G=2, d_n=8, d_v=8, d_r=4, S=17, dtype="f32")
+    inp = W.make_gva_inputs(wl, seed=52)
+    got = O.gva_decode_multi_step(inp.V, inp.kr, inp.q_nope[:, None], inp.q_rope[:, None], inp.M,
+                                  inp.lens, wl.scale, 10000.0, "f32")
+    ref = O.gva_decode_step(inp.V, inp.kr, inp.q_nope, inp.q_rope, inp.M, inp.lens, wl.scale,
+                            10000.0, "f32")
+    assert np.array_equal(got[:, 0], ref)
