@@ -58,7 +58,7 @@ def parse():
     p.add_argument("--profile-copy-mb", type=int, default=0,
                    help="with --profile-step/--profile-decode: first run a plain elementwise copy "
                         "(read N MiB, write N MiB) three times, the reference for traffic counters")
-    p.add_argument("--mode", choices=["step", "gqa", "folded", "multi"], default="step")
+    p.add_argument("--mode", choices=["step", "gqa", "folded", "multi", "lifecycle"], default="step")
     return p.parse_args()
 
 
@@ -90,6 +90,9 @@ def main():
         return
     if args.mode == "multi":
         multi_compare(args)
+        return
+    if args.mode == "lifecycle":
+        lifecycle_bench(args)
         return
     wl = W.WORKLOADS[args.workload]
     if args.split >= 0:
@@ -541,6 +544,63 @@ def multi_compare(args):
                           "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4),
                           "query_tokens_per_s": round(wl.B * nq / us * 1e6, 1)}
     print(json.dumps(res), flush=True)
+
+
+def lifecycle_bench(args):
+    """`--mode lifecycle`: paged-cache block copies (copy-on-write of 1024
+    blocks of 64 tokens: every V row of 4 groups and the positional keys, read
+    and written once), and the launch cost of fork (64 sequences) and rollback,
+    each as K launches in one graph."""
+    import numpy as np
+    import torch
+
+    import compact_kv_cache_amd as gva
+
+    dev = torch.device("cuda:0")
+    K = args.steps
+    B, n_pairs, nblk = 64, 1024, 4096
+    shape = gva.make_shape(B, 16, 4, 64, 64, 16, max_seq_len=64 * 64, block_size=64, num_blocks=nblk,
+                           max_blocks_per_seq=64, dtype="bf16")
+    v = torch.randn(nblk, 4, 64, 64, device=dev).bfloat16()
+    k = torch.randn(nblk, 64, 16, device=dev).bfloat16()
+    table = torch.arange(B * 64, dtype=torch.int32, device=dev).view(B, 64).contiguous()
+    seq = torch.full((B,), 1000, dtype=torch.int32, device=dev)
+    perm = np.random.Generator(np.random.PCG64(7)).permutation(nblk).astype(np.int32)
+    pairs = [(torch.tensor(perm[i * 2 * n_pairs:(i * 2 + 1) * n_pairs], device=dev),
+              torch.tensor(perm[(i * 2 + 1) * n_pairs:(i * 2 + 2) * n_pairs], device=dev)) for i in range(2)]
+    zero = torch.zeros(B, dtype=torch.int32, device=dev)
+    src_s = torch.arange(0, B // 2, dtype=torch.int32, device=dev)
+    dst_s = torch.arange(B // 2, B, dtype=torch.int32, device=dev)
+
+    def gtime(fn):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K * 1e3
+
+    block_bytes = 4 * 64 * 64 * 2 + 64 * 16 * 2
+    us_copy = gtime(lambda i: gva.gva_copy_blocks(shape, pairs[i % 2][0], pairs[i % 2][1], v, k))
+    us_fork = gtime(lambda i: gva.gva_fork(shape, src_s, dst_s, seq, table))
+    us_roll = gtime(lambda i: gva.gva_rollback(shape, seq, zero))
+    moved = 2 * n_pairs * block_bytes  # read + write
+    print(json.dumps({
+        "mode": "lifecycle",
+        "config": {"workload": f"paged bf16 cache, {nblk} blocks of 64 tokens (G=4, d_v=64, d_r=16, "
+                               f"{block_bytes} B per block); copy {n_pairs} blocks; fork 32 of 64 sequences",
+                   "steps": K},
+        "copy_blocks_us": round(us_copy, 3), "copy_bytes_moved": moved,
+        "copy_GBps": round(moved / us_copy / 1e3, 1), "copy_frac": round(moved / us_copy / 1e3 / HBM_PEAK_GBPS, 4),
+        "fork_us": round(us_fork, 3), "rollback_us": round(us_roll, 3)}), flush=True)
 
 
 def measure_gva_vs_gqa(wl, K: int) -> dict:

@@ -18,7 +18,7 @@ __all__ = [
     "GvaShape", "GVA_F32", "GVA_BF16", "GvaError", "make_shape", "lib",
     "gva_append", "gva_rope_query", "gva_decode", "gva_decode_step", "gva_gqa_ref_decode",
     "gva_fold_query_projection", "gva_query_projection", "gva_rope_query_multi", "gva_decode_multi",
-    "gva_decode_multi_workspace_bytes",
+    "gva_decode_multi_workspace_bytes", "gva_copy_blocks", "gva_fork", "gva_rollback",
     "gva_decode_workspace_bytes", "gva_decode_step_workspace_bytes", "gva_decode_split_tokens", "gva_cache_bytes_per_token",
     "gva_status_string", "gva_abi_version", "workspace_for",
 ]
@@ -138,6 +138,36 @@ def gva_decode_multi(shape: GvaShape, n_q: int, q_nope, q_rope, M, v_cache, kr_c
 
 def gva_decode_multi_workspace_bytes(shape: GvaShape, n_q: int) -> int:
     return int(lib.gva_decode_multi_workspace_bytes(shape, int(n_q)))
+
+
+def gva_copy_blocks(shape: GvaShape, src_blocks, dst_blocks, v_cache, kr_cache, block_table=None,
+                    remap_seqs=None, remap_slots=None, stream=None) -> None:
+    """Copy whole 64-token blocks (int32 device index tensors); with remap_seqs
+    and remap_slots also point those block-table slots at the copies."""
+    dt = _TORCH.get(shape.dtype)
+    n = int(src_blocks.numel())
+    if int(dst_blocks.numel()) != n or (remap_seqs is not None and int(remap_seqs.numel()) != n):
+        raise ValueError("index tensors must have the same length")
+    _check(lib.gva_copy_blocks(shape, _ptr(src_blocks, torch.int32, "src_blocks"),
+                               _ptr(dst_blocks, torch.int32, "dst_blocks"), n,
+                               _ptr(remap_seqs, torch.int32, "remap_seqs"),
+                               _ptr(remap_slots, torch.int32, "remap_slots"), _ptr(v_cache, dt, "v_cache"),
+                               _ptr(kr_cache, dt, "kr_cache"), _ptr(block_table, torch.int32, "block_table"),
+                               _stream(stream)), "gva_copy_blocks")
+
+
+def gva_fork(shape: GvaShape, src_seqs, dst_seqs, seq_lens, block_table, stream=None) -> None:
+    n = int(src_seqs.numel())
+    if int(dst_seqs.numel()) != n:
+        raise ValueError("src_seqs and dst_seqs must have the same length")
+    _check(lib.gva_fork(shape, _ptr(src_seqs, torch.int32, "src_seqs"), _ptr(dst_seqs, torch.int32, "dst_seqs"),
+                        n, _ptr(seq_lens, torch.int32, "seq_lens"),
+                        _ptr(block_table, torch.int32, "block_table"), _stream(stream)), "gva_fork")
+
+
+def gva_rollback(shape: GvaShape, seq_lens, n_drop, stream=None) -> None:
+    _check(lib.gva_rollback(shape, _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(n_drop, torch.int32, "n_drop"),
+                            _stream(stream)), "gva_rollback")
 
 
 def gva_fold_query_projection(M, wq_nope, w_fold, stream=None) -> None:

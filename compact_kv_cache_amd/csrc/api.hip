@@ -382,6 +382,57 @@ gva_status gva_query_projection(const gva_shape* shape, int32_t d_model, const v
   return hip_status(gva::launch_project(a, stream), "gva_query_projection launch");
 }
 
+gva_status gva_copy_blocks(const gva_shape* shape, const int32_t* src_blocks, const int32_t* dst_blocks,
+                           int32_t n_pairs, const int32_t* remap_seqs, const int32_t* remap_slots, void* v_cache,
+                           void* kr_cache, int32_t* block_table, hipStream_t stream) {
+  gva_status st = check_shape(shape, false);
+  if (st != GVA_OK) return st;
+  if (shape->block_size != 64) return fail(GVA_ERR_INVALID_ARGUMENT, "block copies need a paged cache");
+  if (n_pairs < 0 || n_pairs > 65535) return fail(GVA_ERR_INVALID_ARGUMENT, "n_pairs = %d out of range", n_pairs);
+  if (n_pairs == 0) return ok();
+  if (!src_blocks || !dst_blocks || !v_cache)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "src_blocks, dst_blocks and v_cache must be non-NULL");
+  if (shape->d_r > 0 && !kr_cache) return fail(GVA_ERR_INVALID_ARGUMENT, "kr_cache must be non-NULL when d_r > 0");
+  if ((remap_seqs == nullptr) != (remap_slots == nullptr) || (remap_seqs && !block_table))
+    return fail(GVA_ERR_INVALID_ARGUMENT, "remap_seqs, remap_slots and block_table go together");
+  const int es = shape->dtype == GVA_BF16 ? 2 : 4;
+  gva::CopyBlocksLaunch a{};
+  a.B = shape->B;
+  a.num_blocks = shape->num_blocks;
+  a.max_blocks = shape->max_blocks_per_seq;
+  a.n_pairs = n_pairs;
+  a.v_block_bytes = (int64_t)shape->G * 64 * shape->d_v * es;
+  a.kr_block_bytes = (int64_t)64 * shape->d_r * es;
+  a.src = src_blocks;
+  a.dst = dst_blocks;
+  a.remap_seqs = remap_seqs;
+  a.remap_slots = remap_slots;
+  a.v_cache = v_cache;
+  a.kr_cache = kr_cache;
+  a.block_table = block_table;
+  return hip_status(gva::launch_copy_blocks(a, stream), "gva_copy_blocks launch");
+}
+
+gva_status gva_fork(const gva_shape* shape, const int32_t* src_seqs, const int32_t* dst_seqs, int32_t n,
+                    int32_t* seq_lens, int32_t* block_table, hipStream_t stream) {
+  gva_status st = check_shape(shape, false);
+  if (st != GVA_OK) return st;
+  if (shape->block_size != 64) return fail(GVA_ERR_INVALID_ARGUMENT, "fork needs a paged cache");
+  if (n < 0 || n > 65535) return fail(GVA_ERR_INVALID_ARGUMENT, "n = %d out of range", n);
+  if (n == 0) return ok();
+  if (!src_seqs || !dst_seqs || !seq_lens || !block_table)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "src_seqs, dst_seqs, seq_lens and block_table must be non-NULL");
+  gva::ForkLaunch a{shape->B, shape->max_blocks_per_seq, n, src_seqs, dst_seqs, seq_lens, block_table};
+  return hip_status(gva::launch_fork(a, stream), "gva_fork launch");
+}
+
+gva_status gva_rollback(const gva_shape* shape, int32_t* seq_lens, const int32_t* n_drop, hipStream_t stream) {
+  gva_status st = check_shape(shape, false);
+  if (st != GVA_OK) return st;
+  if (!seq_lens || !n_drop) return fail(GVA_ERR_INVALID_ARGUMENT, "seq_lens and n_drop must be non-NULL");
+  return hip_status(gva::launch_rollback(seq_lens, n_drop, shape->B, stream), "gva_rollback launch");
+}
+
 size_t gva_decode_multi_workspace_bytes(const gva_shape* shape, int32_t n_q) {
   if (check_shape(shape, false) != GVA_OK || n_q < 1) return 0;
   return workspace_for(shape, n_q);

@@ -128,6 +128,29 @@ struct ProjectLaunch {
   void* q_rope;        // [B][H][d_r]
 };
 
+// Paged-cache lifecycle.
+struct CopyBlocksLaunch {
+  int B, num_blocks, max_blocks, n_pairs;
+  int64_t v_block_bytes, kr_block_bytes;  // bytes of one block in each cache
+  const int32_t* src;
+  const int32_t* dst;
+  const int32_t* remap_seqs;   // optional (copy-on-write table update)
+  const int32_t* remap_slots;
+  void* v_cache;
+  void* kr_cache;
+  int32_t* block_table;
+};
+struct ForkLaunch {
+  int B, max_blocks, n;
+  const int32_t* src;
+  const int32_t* dst;
+  int32_t* seq_lens;
+  int32_t* block_table;
+};
+
+hipError_t launch_copy_blocks(const CopyBlocksLaunch& a, hipStream_t s);
+hipError_t launch_fork(const ForkLaunch& a, hipStream_t s);
+hipError_t launch_rollback(int32_t* seq_lens, const int32_t* n_drop, int B, hipStream_t s);
 hipError_t launch_fold(const FoldLaunch& a, hipStream_t s);
 hipError_t launch_project(const ProjectLaunch& a, hipStream_t s);
 hipError_t launch_append(const AppendLaunch& a, hipStream_t s);

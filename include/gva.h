@@ -245,6 +245,42 @@ gva_status gva_decode_step(const gva_shape* shape, const void* v_new, const void
 size_t gva_decode_step_workspace_bytes(const gva_shape* shape);
 
 /*
+ * Cache lifecycle on the paged cache (block_size == 64). The [gqa] page
+ * (与位置编码和 KV Cache 的关系) lists what an engine does with cache blocks for
+ * beam search, speculative decoding and prefix sharing: copy, share, commit
+ * or roll back. The caller keeps the block allocator; these calls do the
+ * device-side work. All index arrays are int32 device arrays.
+ *
+ * gva_copy_blocks - block dst_blocks[i] := block src_blocks[i] for
+ * i < n_pairs: the V rows of all G groups and the 64 positional-key rows.
+ * With remap_seqs / remap_slots (both or neither), block_table[remap_seqs[i]]
+ * [remap_slots[i]] is then set to dst_blocks[i]: copy-on-write of a shared
+ * block in one call. Destinations must be distinct and not among the
+ * sources; pairs with a block id outside [0, num_blocks) are skipped.
+ */
+gva_status gva_copy_blocks(const gva_shape* shape, const int32_t* src_blocks, const int32_t* dst_blocks,
+                           int32_t n_pairs, const int32_t* remap_seqs, const int32_t* remap_slots, void* v_cache,
+                           void* kr_cache, int32_t* block_table, hipStream_t stream);
+
+/*
+ * gva_fork - sequence dst_seqs[i] takes the block-table row and the length of
+ * sequence src_seqs[i] (i < n): its blocks become shared. Before a forked
+ * sequence appends into a shared, partly filled block, the caller copies it
+ * (gva_copy_blocks with remap). Destinations must be distinct and not among
+ * the sources; out-of-range or equal indices are skipped.
+ */
+gva_status gva_fork(const gva_shape* shape, const int32_t* src_seqs, const int32_t* dst_seqs, int32_t n,
+                    int32_t* seq_lens, int32_t* block_table, hipStream_t stream);
+
+/*
+ * gva_rollback - drop the newest tokens: seq_lens[b] -= n_drop[b] for every
+ * sequence (n_drop int32 [B]; negative values count as 0; lengths stop at 0),
+ * e.g. the rejected tokens of a speculative step. The dropped rows stay in the
+ * cache and are overwritten by the next appends. Works for both layouts.
+ */
+gva_status gva_rollback(const gva_shape* shape, int32_t* seq_lens, const int32_t* n_drop, hipStream_t stream);
+
+/*
  * gva_fold_query_projection - fold the reconstruction maps into the query
  * projection, once per model ([digest] section 与现有产品 / 工作流的接口: at
  * inference the reconstruction matrix can be folded into the query projection
