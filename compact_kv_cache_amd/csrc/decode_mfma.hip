@@ -48,9 +48,10 @@
 // positional key and the query slice are rotated in the prologue with the same
 // routine as gva_append / gva_rope_query, split-0 workgroups
 // store the new rows, and the workgroup whose tile holds the new position
-// substitutes that row. Every workgroup of the sequence takes a ticket after
-// reading seq_lens[b]; the last ticket stores the new length, so no workgroup
-// can observe it mid-call. Results equal the three separate calls bit for bit.
+// substitutes that row. The new length is stored by the last arrival on a
+// per-sequence counter that every workgroup reaches only after reading
+// seq_lens[b], so no workgroup can observe it mid-call. Results equal the
+// three separate calls bit for bit.
 #include "gva_device.hpp"
 #include "launch.hpp"
 
@@ -295,20 +296,26 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   const int n = min(n_full, a.max_seq_len);
   const int n_parts = (n + a.split - 1) / a.split;
 
-  // Fused step: a workgroup takes its ticket only after a barrier that
-  // follows every wave's read of seq_lens[b] (the barrier waits for the scalar
-  // read to return). The last of the sequence's G * n_split tickets stores the
-  // new length, which therefore cannot be observed by any workgroup of this
-  // call. Participating workgroups take the ticket once their tile stream is
-  // under way, so its round trip hides under the tile loads.
+  // Fused step: the new length is stored only once every workgroup of the
+  // sequence has read the old one. Arrivals on the sequence's counter come
+  // from each group's finalizer (the workgroup that writes the group's
+  // output: the only participant, or the last to arrive for the split-K
+  // merge, which every other participant reaches first) and from every
+  // workgroup whose partition lies past the stored length (after a barrier
+  // that follows its waves' reads). The last of these G * (1 + n_split -
+  // max(n_parts, 1)) arrivals stores the new length and clears the counter;
+  // no workgroup of the call reads seq_lens[b] after it. The arrival is one
+  // atomic per finalizer at the end, issued ahead of the merge loads, so that
+  // no atomic sits between the tile loads of a wave.
+  const int seq_arrivals = G * (1 + a.n_split - max(n_parts, 1));
   int ticket = 0;
-  auto take_ticket = [&]() {
-    if (tid == 0)
+  auto arrive_seq = [&]() {  // thread 0
+    if constexpr (STEP)
       ticket = __hip_atomic_fetch_add(a.counters_seq + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  auto finish_step = [&]() {
+  auto finish_step = [&]() {  // thread 0, after arrive_seq
     if constexpr (STEP) {
-      if (tid == 0 && ticket == G * a.n_split - 1) {
+      if (ticket == seq_arrivals - 1) {
         a.seq_lens_rw[b] = n_full;
         __hip_atomic_store(a.counters_seq + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -317,8 +324,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   if (split >= max(n_parts, 1)) {  // uniform per workgroup; its tile loads are simply dropped
     if constexpr (STEP) {
       __syncthreads();
-      take_ticket();
-      finish_step();
+      if (tid == 0) {
+        arrive_seq();
+        finish_step();
+      }
     }
     return;
   }
@@ -466,8 +475,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       }
     }
   }
-
-  if constexpr (STEP) take_ticket();
 
   // Selection fragments: sel[par] picks channel 16*db + col out of the 32
   // channels of half db/2 (par = db % 2).
@@ -641,10 +648,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   }
   __bf16* out = reinterpret_cast<__bf16*>(a.out);
   if (n_parts <= 1) {
+    if (tid == 0) arrive_seq();
 #pragma unroll
     for (int u = 0; u < kPer; ++u)
       if ((tid >> 6) + u * kWaves < NCOL) out[orow[u] * kD + d] = (__bf16)(l[u] > 0.f ? o[u] / l[u] : 0.f);
-    finish_step();
+    if (tid == 0) finish_step();
     return;
   }
 #pragma unroll
@@ -660,13 +668,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   }
   int32_t* counter = a.counters + (int64_t)b * G + g;
   if (arrive_last(counter, n_parts)) {
+    if (tid == 0) arrive_seq();
 #pragma unroll
     for (int u = 0; u < kPer; ++u)
       if ((tid >> 6) + u * kWaves < NCOL)
         out[orow[u] * kD + d] = (__bf16)merge_partials(a.ws_o, a.ws_ml, orow[u] * a.n_split, n_parts, d);
-    if (tid == 0) reset_counter(counter);
+    if (tid == 0) {
+      reset_counter(counter);
+      finish_step();
+    }
   }
-  finish_step();
 }
 
 template <int HPG, int KR, bool GQA, bool STEP, int NQ>
