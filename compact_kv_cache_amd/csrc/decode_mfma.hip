@@ -131,6 +131,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   const int col = lane & 15, r = lane >> 4;                 // MFMA column / lane group
   const int H = a.H, G = a.G, d_r = a.d_r;
 
+  // Fused step: waves 4..7 rotate the group's query slices (pairs
+  // 0 .. HPG*d_r/2-1) and the appended key (the next d_r/2 pairs), exactly as
+  // gva_rope_query and gva_append do.
+  constexpr int half = 4 * (KR > 0 ? KR : 1);  // rotation pairs per row (d_r / 2)
+  const int rot_i = (w - 4) * 64 + lane;  // pair handled by this lane (waves 4..7)
+  const bool rot_q = STEP && DR && w >= 4 && rot_i < HPG * half;
+  const bool rot_k = STEP && DR && w >= 4 && !rot_q && rot_i < HPG * half + half;
+  const int rot_j = rot_q ? rot_i / half : 0;  // head within the group
+  const int rot_p = rot_q ? rot_i % half : (rot_k ? rot_i - HPG * half : 0);  // pair index
+
   // Workgroup id -> (sequence, partition) pair p and group g; the G groups of a
   // pair share id % 8 (one XCD) and have consecutive slots there.
   const int pairs = a.B * a.n_split;
@@ -202,18 +212,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   // it is kept in LDS, not in registers, for the one tile that holds it.
   u32x4 vnew_l = u32x4{0u, 0u, 0u, 0u};
   if constexpr (STEP) vnew_l = ld16(reinterpret_cast<const __bf16*>(a.v_new) + ((int64_t)b * G + g) * kD, 8 * (lane & 7));
-  // Fused step: waves 4..7 rotate the group's query slices (pairs
-  // 0 .. HPG*d_r/2-1) and the appended key (the next d_r/2 pairs), exactly as
-  // gva_rope_query and gva_append do. Every lane loads one bf16 pair of each
-  // source (lanes with no pair re-read a valid one) and selects afterwards: a
-  // per-lane choice of pointer would be compiled into a vector load of the
-  // kernel argument, queued behind the tile loads.
-  const int half = d_r / 2;
-  const int rot_i = (w - 4) * 64 + lane;  // pair handled by this lane (waves 4..7)
-  const bool rot_q = STEP && DR && w >= 4 && rot_i < HPG * half;
-  const bool rot_k = STEP && DR && w >= 4 && !rot_q && rot_i < HPG * half + half;
-  const int rot_j = rot_q ? rot_i / half : 0;  // head within the group
-  const int rot_p = rot_q ? rot_i % half : (rot_k ? rot_i - HPG * half : 0);  // pair index
+  // Fused step: every lane loads one bf16 pair of each rotation source (lanes
+  // with no pair re-read a valid one) and selects afterwards: a per-lane
+  // choice of pointer would be compiled into a vector load of the kernel
+  // argument, queued behind the tile loads.
   uint32_t rx = 0;
   if constexpr (STEP && DR) {
     const __bf16* qsrc = reinterpret_cast<const __bf16*>(a.q_rope) + ((int64_t)b * H + g * HPG + rot_j) * d_r;
@@ -305,16 +307,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   // that follows its waves' reads). The last of these G * (1 + n_split -
   // max(n_parts, 1)) arrivals stores the new length and clears the counter;
   // no workgroup of the call reads seq_lens[b] after it. The arrival is one
-  // atomic per finalizer at the end, issued ahead of the merge loads, so that
-  // no atomic sits between the tile loads of a wave.
+  // atomic per finalizer at the end, made by the first lane of the last wave,
+  // which has no merge loads of its own (loads of a wave complete in order, so
+  // an atomic ahead of them would delay them by its round trip).
+  static_assert(!STEP || NCOL < kWaves, "the last wave is free during the merge");
+  constexpr int kSeqThread = 64 * (kWaves - 1);
   const int seq_arrivals = G * (1 + a.n_split - max(n_parts, 1));
-  int ticket = 0;
-  auto arrive_seq = [&]() {  // thread 0
-    if constexpr (STEP)
-      ticket = __hip_atomic_fetch_add(a.counters_seq + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  auto finish_step = [&]() {  // thread 0, after arrive_seq
+  auto arrive_seq = [&]() {  // thread kSeqThread
     if constexpr (STEP) {
+      const int ticket =
+          __hip_atomic_fetch_add(a.counters_seq + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (ticket == seq_arrivals - 1) {
         a.seq_lens_rw[b] = n_full;
         __hip_atomic_store(a.counters_seq + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -324,10 +326,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   if (split >= max(n_parts, 1)) {  // uniform per workgroup; its tile loads are simply dropped
     if constexpr (STEP) {
       __syncthreads();
-      if (tid == 0) {
-        arrive_seq();
-        finish_step();
-      }
+      if (tid == kSeqThread) arrive_seq();
     }
     return;
   }
@@ -425,7 +424,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       const float x1 = __uint_as_float(rx & 0xffff0000u);
       const double at = rot_q ? (double)max(n_full - 1, 0) : (double)pos;
       __bf16* dst = rot_q ? &qrot_sh[rot_j][2 * rot_p] : &krot_sh[2 * rot_p];
-      rope_store<__bf16>(x0, x1, at, rope_theta(a.rope, rot_p), dst[0], dst[1]);
+      // (the frequency table is read here, after the tile requests: read
+      // before them, its scalar-cache miss holds the first request back)
+      rope_store<__bf16>(x0, x1, at, rope_theta<half>(a.rope, rot_p), dst[0], dst[1]);
     }
   }
   __syncthreads();
@@ -648,11 +649,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   }
   __bf16* out = reinterpret_cast<__bf16*>(a.out);
   if (n_parts <= 1) {
-    if (tid == 0) arrive_seq();
+    if (tid == kSeqThread) arrive_seq();
 #pragma unroll
     for (int u = 0; u < kPer; ++u)
       if ((tid >> 6) + u * kWaves < NCOL) out[orow[u] * kD + d] = (__bf16)(l[u] > 0.f ? o[u] / l[u] : 0.f);
-    if (tid == 0) finish_step();
     return;
   }
 #pragma unroll
@@ -668,15 +668,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   }
   int32_t* counter = a.counters + (int64_t)b * G + g;
   if (arrive_last(counter, n_parts)) {
-    if (tid == 0) arrive_seq();
+    if (tid == kSeqThread) arrive_seq();
 #pragma unroll
     for (int u = 0; u < kPer; ++u)
       if ((tid >> 6) + u * kWaves < NCOL)
         out[orow[u] * kD + d] = (__bf16)merge_partials(a.ws_o, a.ws_ml, orow[u] * a.n_split, n_parts, d);
-    if (tid == 0) {
-      reset_counter(counter);
-      finish_step();
-    }
+    if (tid == 0) reset_counter(counter);
   }
 }
 

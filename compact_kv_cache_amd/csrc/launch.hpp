@@ -24,10 +24,12 @@ inline RopeTable make_rope_table(double base, int d_r) {
 // empty asm statement keeps each value in a scalar register: without it the
 // compiler folds the selection into a lane-indexed read of the kernel
 // argument, a vector memory load that waits behind every load issued before.
+template <int N = 16>
 __device__ __forceinline__ double rope_theta(const RopeTable& t, int i) {
+  static_assert(N >= 1 && N <= 16, "table size");
   double th = 0.0;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
+  for (int k = 0; k < N; ++k) {
     double v = t.theta[k];
     asm volatile("" : "+s"(v));
     th = (i == k) ? v : th;
