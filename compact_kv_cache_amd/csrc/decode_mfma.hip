@@ -22,17 +22,17 @@
 // the tile to its own LDS buffer (16-byte chunks XOR-swizzled per row) and
 // reads the matrix-core operands back from there. The first tile of every
 // wave is requested from the host bound max_seq_len, before the stored length
-// has arrived; rows past the stored end are cleared when the operands are read.
+// has arrived; rows past the stored end are cleared when the tile is staged.
 //
 // Per wave and 16-token sub-tile, all on v_mfma_f32_16x16x32_bf16:
 //   scores     S^T[tok][col] = V[tok][:] . q'[head(col)][:] + k_r[tok] . q_rope:
 //              A = V rows (lane l: token l%16, 8 channels), B = queries with
 //              the group's heads repeated across the 16 columns; q' is
 //              accumulated in fp32 and rounded to bf16 once.
-//   transpose  C[tok][c] = V[tok][:] . E[:][c], E a 0/1 selection of 16
-//              channels: V^T in the A layout of the next product, exactly.
 //   P.V        O^T[ch][col] += V^T[ch][tok] . P^T[tok][col] over 32 tokens; B =
-//              the score accumulator itself after the softmax, in bf16.
+//              the score accumulator itself after the softmax, in bf16; A =
+//              V^T read from the staged tile with the LDS transpose load
+//              (ds_read_b64_tr_b16), no data movement through the ALUs.
 // Softmax: scores stay unscaled; p = 2^(scale*log2(e)*(s - m_ref)) with one FMA
 // and the raw v_exp_f32. The reference max m_ref only moves when a tile's max
 // exceeds it by more than 2^8 in probability units, so the output rescale is
@@ -61,6 +61,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 union Frag {
   bf16x8 v;
@@ -338,7 +340,19 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   // Registers -> LDS stage (plain contiguous stores), then the operand
   // fragments back. LDS operations of one wave complete in order, so the
   // fragments see the stage and the next stage cannot overtake them.
-  auto stage = [&](const Tile<GQA, KR>& T) {
+  // Rows at or past the stored end (a first-round tile may hold stale or
+  // unwritten cache rows there) are staged as zeros: their scores are masked,
+  // and zero value rows keep the probability-weighted sum exact.
+  auto stage = [&](Tile<GQA, KR>& T) {
+    if (!(T.ok && T.t0 + kTile <= t_end)) {  // wave-uniform
+      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool past = T.t0 + 8 * i + (lane >> 3) >= t_end;
+        T.sa[i] = past ? z : T.sa[i];
+        if constexpr (GQA) T.vb[i] = past ? z : T.vb[i];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       *reinterpret_cast<u32x4*>(stage_w + 1024 * i + 16 * lane) = T.sa[i];
@@ -364,32 +378,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       }
       if constexpr (DR) F.kr[st].u = *reinterpret_cast<const u32x4*>(stage_w + 8192 + row * (16 * KR) + 2 * kr_off);
     }
-    // Rows at or past the stored end (a first-round tile may hold stale or
-    // unwritten cache rows there) become zeros: their scores are masked, and
-    // zero rows keep the probability-weighted sum exact.
-    if (!F.full) {
-      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bool past = T.t0 + 16 * st + col >= t_end;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          F.sa[st][h].u = past ? z : F.sa[st][h].u;
-        }
-        if constexpr (DR) F.kr[st].u = past ? z : F.kr[st].u;
-      }
-    }
   };
 
-  // GQA value rows of sub-tile st, channels 32*h + 8*r .. +7, from the stage
-  // (rows at or past the stored end read as zeros).
-  auto value_rows = [&](const Frags<DR>& T, int st, int h) {
-    const int row = 16 * st + col;
-    Frag f;
-    f.u = *reinterpret_cast<const u32x4*>(stage_w + 8192 + row * (kD * 2) + 16 * ((4 * h + r) ^ stage_swizzle(row)));
-    if (!T.full && T.t0 + row >= t_end) f.u = u32x4{0u, 0u, 0u, 0u};
-    return f;
-  };
 
   // ---- queries --------------------------------------------------------------------
   // query slots past d_r contribute nothing (masked after the tile issue, so
@@ -477,14 +467,25 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     }
   }
 
-  // Selection fragments: sel[par] picks channel 16*db + col out of the 32
-  // channels of half db/2 (par = db % 2).
-  Frag sel[2];
+  // V^T operand of P.V through the LDS transpose load. Within each 16-lane
+  // group r, ds_read_b64_tr_b16 hands lane col element e of the 8-byte chunk
+  // addressed by lane 4*e + col/4 (its element col % 4). So lane j addresses
+  // staged token 4*r + j/4 (+ 16*h + 32*pr) and channels 16*db + 4*(j%4)
+  // .. +3, and lane col receives channel 16*db + col of four consecutive
+  // tokens: the rows of V^T in the A layout, in the token order of the score
+  // accumulator used as B (tokens 4r..4r+3 of sub-tile 2pr, then of 2pr+1).
+  // Adding a multiple of 16 to the row leaves its swizzle unchanged, so one
+  // per-lane offset per db serves every (pr, h).
+  int tr_off[4];
+  {
+    const int row = 4 * r + (col >> 2);
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      sel[par].h[e] = (__bf16)((r == 2 * par + (col >> 3) && e == (col & 7)) ? 1.f : 0.f);
+    for (int db = 0; db < 4; ++db) {
+      const int chan = 16 * db + 4 * (col & 3);
+      tr_off[db] = row * (kD * 2) + 16 * ((chan >> 3) ^ stage_swizzle(row)) + 2 * (chan & 7);
+    }
+  }
+  const char* const vstage = stage_w + (GQA ? 8192 : 0);
 
   // ---- streaming ------------------------------------------------------------------
   f32x4 acc_o[4];
@@ -509,6 +510,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
             T.sa[st][1] = v1;
             if constexpr (DR) T.kr[st] = kk;
           }
+        }
+        // ... and in the staged row that the value operand is read from
+        if (pos < t_end && lane < kD / 8) {
+          const int prow = pos - T.t0;
+          *reinterpret_cast<u32x4*>(stage_w + prow * (kD * 2) + 16 * (lane ^ stage_swizzle(prow))) =
+              *reinterpret_cast<const u32x4*>(vnew_sh + 8 * lane);
         }
       }
     }
@@ -568,19 +575,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       }
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        f32x4 ca, cb;
-        if constexpr (GQA) {
-          ca = mma(value_rows(T, 2 * pr, db >> 1), sel[db & 1], kZero4);
-          cb = mma(value_rows(T, 2 * pr + 1, db >> 1), sel[db & 1], kZero4);
-        } else {
-          ca = mma(T.sa[2 * pr][db >> 1], sel[db & 1], kZero4);
-          cb = mma(T.sa[2 * pr + 1][db >> 1], sel[db & 1], kZero4);
-        }
         Frag vt;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vt.h[i] = (__bf16)ca[i];
-          vt.h[4 + i] = (__bf16)cb[i];
+        for (int h = 0; h < 2; ++h) {
+          const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vstage + tr_off[db] + (32 * pr + 16 * h) * (kD * 2)));
+          const uint2 xb = __builtin_bit_cast(uint2, x);
+          vt.u[2 * h] = xb.x;
+          vt.u[2 * h + 1] = xb.y;
         }
         acc_o[db] = mma(vt, pb, acc_o[db]);
       }
