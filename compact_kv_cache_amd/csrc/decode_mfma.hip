@@ -74,6 +74,24 @@ __device__ __forceinline__ f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
 }
 
+// Max / sum over the four 16-lane rows of the wave (lanes l, l^16, l^32,
+// l^48) with the gfx950 row-swap permutes: v_permlane16_swap pairs rows 0-1
+// and 2-3, v_permlane32_swap the two halves; no LDS round trip. Every lane
+// combines the same two operands in the same order, so all four rows end
+// with the same value.
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // 16-byte load; `base` is wave-uniform, `off` a per-lane element offset.
 __device__ __forceinline__ u32x4 ld16(const __bf16* base, int off) {
   return *reinterpret_cast<const u32x4*>(base + off);
@@ -543,8 +561,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[st][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = rows_max(mx);
     const float m_new = (mx > m_ref + thr) ? mx : m_ref;
     if (__any(m_new != m_ref)) {
       // 0 on a column's first tile; 1 where the max does not move (also a
@@ -611,8 +628,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   }
 
   // ---- merge the waves ----------------------------------------------------------------
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = rows_sum(l_run);
   if (col < NCOL) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
