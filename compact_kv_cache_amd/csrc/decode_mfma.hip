@@ -37,10 +37,10 @@
 // and the raw v_exp_f32. The reference max m_ref only moves when a tile's max
 // exceeds it by more than 2^8 in probability units, so the output rescale is
 // rare and p stays below 256.
-// Loads are non-temporal, from a wave-uniform tile base plus per-lane offsets;
-// rows past the end are clamped and a missing page reads the first row, so no
-// load is ever predicated and the next tile's loads stay in flight while the
-// current one is computed.
+// Loads are non-temporal buffer loads over a per-tile range: rows past the end
+// and missing pages read as zeros without touching memory, so no load is ever
+// predicated and the next tile's loads stay in flight while the current one
+// is computed.
 //
 // Fused step (the decode loop of the GQA tutorial page, section on cache
 // growth: store the new token's state, then let its query read the cache up to
@@ -102,6 +102,10 @@ __device__ __forceinline__ u32x4 ld16_stream(const __bf16* base, int off) {
 }
 
 constexpr f32x4 kZero4 = {0.f, 0.f, 0.f, 0.f};
+// Buffer resource word 3 for raw (untyped, unswizzled) loads: 32-bit data
+// format, the value the gfx9-family matrix-core libraries use.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;  // cache-policy bit: non-temporal (streamed once)
 constexpr int kWaves = 8;            // waves per workgroup
 constexpr float kRescaleLog2 = 8.f;  // move the reference max only beyond 2^8
 
@@ -115,7 +119,7 @@ struct Tile {
   u32x4 vb[GQA ? 8 : 1];
   u32x4 kr[KR > 0 ? KR : 1];
   int t0;     // first token of the tile
-  int bound;  // last row of the tile that was read (rows past it re-read it)
+  int bound;  // last row of the tile that was read (rows past it load as zeros)
   bool ok;    // tile exists and its page is valid (wave-uniform)
 };
 
@@ -252,7 +256,21 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   __shared__ __attribute__((aligned(16))) char stage_lds[kWaves * kStageBytes];
   char* const stage_w = stage_lds + w * kStageBytes;
 
-  // Tile k of this partition, rows clamped to [t_begin, t_hi) (t_hi is the
+  // Tile loads are buffer loads: the tile's rows [t0, t_hi) form the range of
+  // a buffer resource, rows past it (and a whole missing tile) load as zeros
+  // without a memory access, and the per-lane offsets are the same for every
+  // tile. Instruction i, lane l fills staged row 8i + l/8, chunk position l%8,
+  // with chunk (l%8) ^ swizzle(row) of that row; swizzle(8i + l/8) =
+  // (l/8) ^ (i&1), so two offsets per 4 KB half (i even, odd) serve all
+  // eight instructions with immediate offsets 1024*(i%4).
+  int voff[2][2];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      voff[hi][par] = 4096 * hi + (lane >> 3) * (kD * 2) + 16 * ((lane & 7) ^ (lane >> 3) ^ par);
+
+  // Tile k of this partition: rows [t0, min(t0 + 64, t_hi)) (t_hi is the
   // partition end from max_seq_len for the first round, the stored end after).
   auto issue = [&](Tile<GQA, KR>& T, int k, int t_hi, int tiles) {
     const int t0 = t_begin + k * kTile;
@@ -269,32 +287,25 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       kbase = ((int64_t)b * a.capacity + t0) * d_r;
     }
     if (!ok) vbase = kbase = 0;
+    const int rows = ok ? min(kTile, t_hi - t0) : 0;
     T.t0 = t0;
     T.ok = ok;
-    // last row this tile may touch: rows past the end re-read it; a missing
-    // tile reads row 0 of the cache
-    const int bound = ok ? min(kTile - 1, t_hi - 1 - t0) : 0;
-    T.bound = bound;
-    // instruction i, lane l fills staged row 8i + l/8, chunk position l%8,
-    // with chunk (l%8) ^ swizzle(row) of cache row min(row, bound)
-    const char* sp = reinterpret_cast<const char*>(sc + vbase);
-    const char* vp = reinterpret_cast<const char*>(vc + vbase);
+    T.bound = max(rows - 1, 0);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(sc + vbase), 0, rows * kD * 2, kBufferWord3);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 8 * i + (lane >> 3);
-      const int off = min(row, bound) * (kD * 2) + 16 * ((lane & 7) ^ stage_swizzle(row));
-      T.sa[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sp + off));
-      if constexpr (GQA) T.vb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + off));
+    for (int i = 0; i < 8; ++i)
+      T.sa[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i >> 2][i & 1] + 1024 * (i & 3), 0, kNonTemporal);
+    if constexpr (GQA) {
+      const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(vc + vbase), 0, rows * kD * 2, kBufferWord3);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        T.vb[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i >> 2][i & 1] + 1024 * (i & 3), 0, kNonTemporal);
     }
     if constexpr (DR) {
-      const char* kp = reinterpret_cast<const char*>(kc + kbase);
+      // 1 KB of positional-key rows (16*KR bytes each) per instruction
+      const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(kc + kbase), 0, rows * 16 * KR, kBufferWord3);
 #pragma unroll
-      for (int i = 0; i < KR; ++i) {
-        const int byte = 1024 * i + 16 * lane;
-        const int row = byte / (16 * KR), in_row = byte % (16 * KR);
-        T.kr[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(kp + min(row, bound) * (16 * KR) + in_row));
-      }
+      for (int i = 0; i < KR; ++i) T.kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * lane + 1024 * i, 0, kNonTemporal);
     }
   };
   Tile<GQA, KR> X;
@@ -609,8 +620,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   // Each tile is staged, its registers are reloaded at once with the tile
   // two rounds ahead, and the math runs on the staged copy.
   // The loop has a single exit and issues both reloads on every path (a
-  // reload past the last tile reads row 0), so the compiler's wait counts for
-  // each tile stay exact across iterations.
+  // reload past the last tile has an empty range: zeros, no memory access),
+  // so the compiler's wait counts for each tile stay exact across iterations.
   Frags<DR> F;
 #pragma clang loop unroll(disable)
   for (int k = w; k < n_tiles; k += 2 * kWaves) {
