@@ -332,7 +332,7 @@ def main():
 
 
 KERNEL_SOURCES = ("compact_kv_cache_amd/csrc/decode_mfma.hip", "compact_kv_cache_amd/csrc/gva_device.hpp",
-                  "compact_kv_cache_amd/csrc/launch.hpp")
+                  "compact_kv_cache_amd/csrc/launch.hpp", "compact_kv_cache_amd/csrc/mfma_common.hpp")
 
 
 def recorded_traffic(workload: str):

@@ -18,7 +18,7 @@ __all__ = [
     "GvaShape", "GVA_F32", "GVA_BF16", "GvaError", "make_shape", "lib",
     "gva_append", "gva_rope_query", "gva_decode", "gva_decode_step", "gva_gqa_ref_decode",
     "gva_fold_query_projection", "gva_query_projection", "gva_rope_query_multi", "gva_decode_multi",
-    "gva_decode_multi_workspace_bytes", "gva_copy_blocks", "gva_fork", "gva_rollback",
+    "gva_decode_multi_workspace_bytes", "gva_prefill", "gva_copy_blocks", "gva_fork", "gva_rollback",
     "gva_decode_workspace_bytes", "gva_decode_step_workspace_bytes", "gva_decode_split_tokens", "gva_cache_bytes_per_token",
     "gva_status_string", "gva_abi_version", "workspace_for",
 ]
@@ -138,6 +138,18 @@ def gva_decode_multi(shape: GvaShape, n_q: int, q_nope, q_rope, M, v_cache, kr_c
 
 def gva_decode_multi_workspace_bytes(shape: GvaShape, n_q: int) -> int:
     return int(lib.gva_decode_multi_workspace_bytes(shape, int(n_q)))
+
+
+def gva_prefill(shape: GvaShape, n_q: int, q_nope, q_rope, M, v_cache, kr_cache, seq_lens, block_table,
+                scale: float, out, stream=None) -> None:
+    """Causal attention of the last n_q cached tokens of every sequence (any n_q;
+    bf16): q_nope [B, n_q, H, d_n], q_rope [B, n_q, H, d_r] rotated, out
+    [B, n_q, H, d_v]."""
+    dt = _TORCH.get(shape.dtype)
+    _check(lib.gva_prefill(shape, int(n_q), _ptr(q_nope, dt, "q_nope"), _ptr(q_rope, dt, "q_rope"),
+                           _ptr(M, dt, "M"), _ptr(v_cache, dt, "v_cache"), _ptr(kr_cache, dt, "kr_cache"),
+                           _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(block_table, torch.int32, "block_table"),
+                           float(scale), _ptr(out, dt, "out"), _stream(stream)), "gva_prefill")
 
 
 def gva_copy_blocks(shape: GvaShape, src_blocks, dst_blocks, v_cache, kr_cache, block_table=None,

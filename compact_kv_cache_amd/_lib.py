@@ -49,6 +49,7 @@ SIGNATURES = {
     "gva_decode_multi": (ctypes.c_int, [_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                         _vp, ctypes.c_size_t, _vp]),
     "gva_decode_multi_workspace_bytes": (ctypes.c_size_t, [_shp, _i32]),
+    "gva_prefill": (ctypes.c_int, [_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp]),
     "gva_copy_blocks": (ctypes.c_int, [_shp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "gva_fork": (ctypes.c_int, [_shp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "gva_rollback": (ctypes.c_int, [_shp, _vp, _vp, _vp]),

@@ -252,6 +252,49 @@ gva_status gva_decode_multi(const gva_shape* shape, int32_t n_q, const void* q_n
   return hip_status(e, "gva_decode launch");
 }
 
+gva_status gva_prefill(const gva_shape* shape, int32_t n_q, const void* q_nope, const void* q_rope,
+                       const void* M, const void* v_cache, const void* kr_cache, const int32_t* seq_lens,
+                       const int32_t* block_table, float scale, void* out, hipStream_t stream) {
+  gva_status st = check_shape(shape, false);
+  if (st != GVA_OK) return st;
+  if (shape->dtype != GVA_BF16)
+    return fail(GVA_ERR_UNSUPPORTED, "gva_prefill is built for bf16 caches only");
+  if (n_q < 1) return fail(GVA_ERR_INVALID_ARGUMENT, "n_q = %d must be >= 1", n_q);
+  if (!q_nope || !v_cache || !seq_lens || !out)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "q_nope, v_cache, seq_lens and out must be non-NULL");
+  if (shape->d_r > 0 && (!q_rope || !kr_cache))
+    return fail(GVA_ERR_INVALID_ARGUMENT, "q_rope and kr_cache must be non-NULL when d_r > 0");
+  if (shape->block_size != 0 && !block_table)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "paged cache needs a block_table");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(GVA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0 (got %g)", (double)scale);
+  gva::PrefillLaunch a{};
+  a.B = shape->B;
+  a.H = shape->H;
+  a.G = shape->G;
+  a.d_r = shape->d_r;
+  a.paged = shape->block_size != 0;
+  a.capacity = a.paged ? 0 : shape->capacity;
+  a.num_blocks = shape->num_blocks;
+  a.max_blocks = shape->max_blocks_per_seq;
+  a.max_seq_len = shape->max_seq_len;
+  a.nq = n_q;
+  const int qw = gva::prefill_queries_per_block(shape->H / shape->G);
+  a.n_qblk = (n_q + qw - 1) / qw;
+  a.q_nope = q_nope;
+  a.q_rope = q_rope;
+  a.M = M;
+  a.v_cache = v_cache;
+  a.kr_cache = kr_cache;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.scale = scale;
+  a.out = out;
+  if ((int64_t)((a.B * a.G + 7) / 8) * 8 * a.n_qblk > INT32_MAX)
+    return fail(GVA_ERR_INVALID_ARGUMENT, "grid too large");
+  return hip_status(gva::launch_prefill_mfma(a, stream), "gva_prefill launch");
+}
+
 gva_status gva_decode_step(const gva_shape* shape, const void* v_new, const void* kr_new,
                            const void* q_nope, const void* q_rope, const void* M, void* v_cache,
                            void* kr_cache, int32_t* seq_lens, const int32_t* block_table, float scale,

@@ -213,6 +213,33 @@ gva_status gva_decode_multi(const gva_shape* shape, int32_t n_q, const void* q_n
 size_t gva_decode_multi_workspace_bytes(const gva_shape* shape, int32_t n_q);
 
 /*
+ * gva_prefill - causal attention of many new tokens at once over the cache
+ * (prefill of a prompt, or of one chunk of it): the same computation as
+ * gva_decode_multi for any n_q, on a kernel built for it ([gqa] section on
+ * cache growth: every token's query reads the tokens before it and itself;
+ * the same page's cache lifecycle starts with the prefill of the prompt).
+ * With n = min(seq_lens[b], max_seq_len), query j of sequence b sits at
+ * position n - n_q + j and attends to the tokens t <= n - n_q + j (none, and a
+ * zero output row, where that is negative). The n_q tokens must already be in
+ * the cache (gva_append with n_new = n_q); with n_q = seq_lens[b] the whole
+ * prompt attends to itself.
+ *   n_q      >= 1 queries per sequence; bf16 only
+ *   q_nope   [B][n_q][H][d_n], or the absorbed queries [B][n_q][H][d_v] when
+ *            M is NULL
+ *   q_rope   [B][n_q][H][d_r] rotated at the queries' positions
+ *            (gva_rope_query_multi with the same n_q); NULL when d_r == 0
+ *   M        [H][d_v][d_n] or NULL (as for gva_decode)
+ *   out      [B][n_q][H][d_v]
+ * Other arguments as for gva_decode. No workspace: every workgroup owns whole
+ * query rows and reads every key tile they need. Returns
+ * GVA_ERR_UNSUPPORTED for an fp32 shape, GVA_ERR_INVALID_ARGUMENT for n_q < 1,
+ * a missing pointer or a bad scale.
+ */
+gva_status gva_prefill(const gva_shape* shape, int32_t n_q, const void* q_nope, const void* q_rope,
+                       const void* M, const void* v_cache, const void* kr_cache, const int32_t* seq_lens,
+                       const int32_t* block_table, float scale, void* out, hipStream_t stream);
+
+/*
  * gva_decode_step - one whole decode step in a single call: append one token
  * per sequence, rotate the query's positional slice, decode. Equivalent, bit
  * for bit, to

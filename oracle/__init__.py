@@ -7,4 +7,4 @@ from .gva_oracle import (append_positional_keys, gqa_decode, gva_decode, gva_dec
                          gqa_scalars_per_token, head_group, kv_cache_bytes,
                          materialized_keys, rope, rope_thetas, round_bf16, round_storage,
                          query_projection, fold_query_projection, gva_layer_decode_step,
-                         gva_decode_multi, gva_decode_multi_step)
+                         gva_decode_multi, gva_decode_multi_step, gva_prefill, gva_prefill_step)

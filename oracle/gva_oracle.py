@@ -265,6 +265,54 @@ def gva_decode_multi_step(V, kr_pre, q_nope, q_rope_pre, M, seq_lens, scale: flo
     return gva_decode_multi(V, kr_rot, q_nope, q_rot, M, seq_lens, scale)
 
 
+def gva_prefill(V, kr, q_nope, q_rope, M, seq_lens, scale: float) -> np.ndarray:
+    """Causal attention of the last n_q cached tokens of every sequence, the
+    whole prompt when n_q = n ([gqa] KV Cache 为什么会不断变大: each token's
+    query reads the tokens before it and itself). Plain definition with
+    materialized keys, per (b, h): K = [V_g M_h | k_r] over the n cached tokens
+    (k_r rotated), Q = [q_nope | q_rope] of the n_q queries (q_rope rotated),
+    query j at position p_j = n - n_q + j; scores scale * Q K^T with the
+    entries t > p_j removed, softmax per row, times V_g. A row with p_j < 0
+    reads nothing and is zero. q_nope [B, n_q, H, d_n], q_rope
+    [B, n_q, H, d_r]; returns [B, n_q, H, d_v] float64."""
+    q_nope = np.asarray(q_nope, dtype=np.float64)
+    q_rope = np.asarray(q_rope, dtype=np.float64)
+    B, nq, H = q_nope.shape[:3]
+    G, _, d_v = np.asarray(V[0]).shape
+    out = np.zeros((B, nq, H, d_v))
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n <= 0:
+            continue
+        pos = n - nq + np.arange(nq)
+        rows = pos >= 0
+        allowed = np.arange(n)[None, :] <= pos[:, None]  # [n_q, n]
+        for h in range(H):
+            g = head_group(h, H, G)
+            Vg = np.asarray(V[b][g, :n, :], dtype=np.float64)
+            K = materialized_keys(Vg, M[h], np.asarray(kr[b])[:n])
+            Q = np.concatenate([q_nope[b, :, h], q_rope[b, :, h]], axis=1)
+            S = np.where(allowed, float(scale) * (Q @ K.T), -np.inf)
+            S = S[rows]
+            E = np.exp(S - S.max(axis=1, keepdims=True))
+            out[b, rows, h] = (E / E.sum(axis=1, keepdims=True)) @ Vg
+    return out
+
+
+def gva_prefill_step(V, kr_pre, q_nope, q_rope_pre, M, seq_lens, scale: float, base: float,
+                     cache_dtype: str) -> np.ndarray:
+    """As gva_prefill from pre-RoPE inputs: the cache holds RoPE_t(k~_r[t])
+    rounded to the cache dtype, query j is rotated at its own position
+    n - n_q + j (float64)."""
+    q_rope_pre = np.asarray(q_rope_pre, dtype=np.float64)
+    nq = q_rope_pre.shape[1]
+    kr_rot = [append_positional_keys(np.asarray(k)[:int(n)], 0, base, cache_dtype)
+              for k, n in zip(kr_pre, seq_lens)]
+    pos = np.maximum(np.asarray(seq_lens, dtype=np.float64)[:, None] - nq + np.arange(nq)[None, :], 0.0)
+    q_rot = rope(q_rope_pre, pos[:, :, None], base)
+    return gva_prefill(V, kr_rot, q_nope, q_rot, M, seq_lens, scale)
+
+
 # ---------------------------------------------------------------------------
 # The query projection, and the maps folded into it ([digest] 与现有产品 /
 # 工作流的接口: at inference the reconstruction matrix can be folded into the

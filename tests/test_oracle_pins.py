@@ -536,3 +536,81 @@ def test_multi_query_single_is_decode():
     ref = O.gva_decode_step(inp.V, inp.kr, inp.q_nope, inp.q_rope, inp.M, inp.lens, wl.scale,
                             10000.0, "f32")
     assert np.array_equal(got[:, 0], ref)
+
+
+def test_prefill_brute_force_causal():
+    """The masked-matrix prefill against scalar loops over the explicit causal
+    mask (including queries before the first cached token, which read nothing)."""
+    wl = W.Workload("pin_prefill", 9, B=2, H=4, G=2, d_n=4, d_v=4, d_r=2, S=0, dtype="f32")
+    lens = np.array([6, 3])
+    inp = W.make_gva_inputs(wl, lens=lens, seed=60)
+    nq = 5
+    rng = np.random.default_rng(61)
+    qn = rng.standard_normal((2, nq, 4, 4))
+    qr = rng.standard_normal((2, nq, 4, 2))
+    got = O.gva_prefill(inp.V, inp.kr, qn, qr, inp.M, lens, 0.3)
+    for b in range(2):
+        n = int(lens[b])
+        for j in range(nq):
+            p = n - nq + j
+            for h in range(4):
+                g = h // 2
+                if p < 0:
+                    assert np.all(got[b, j, h] == 0.0)
+                    continue
+                s = []
+                for t in range(p + 1):
+                    k_c = [sum(inp.V[b][g, t, v] * inp.M[h][v, c] for v in range(4)) for c in range(4)]
+                    dot = sum(k_c[c] * qn[b, j, h, c] for c in range(4))
+                    dot += sum(inp.kr[b][t, c] * qr[b, j, h, c] for c in range(2))
+                    s.append(0.3 * dot)
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                tot = sum(w)
+                for c in range(4):
+                    ref = sum(w[t] * inp.V[b][g, t, c] for t in range(p + 1)) / tot
+                    assert abs(got[b, j, h, c] - ref) < 1e-12
+
+
+def test_prefill_closed_forms_and_causality():
+    """Query 0 of a whole-prompt prefill sees only token 0 (its value row,
+    exactly); constant value rows give that constant; the last query is the
+    plain decode; and changing tokens after position p leaves query p alone."""
+    wl = W.Workload("pin_prefill2", 9, B=2, H=8, G=4, d_n=8, d_v=8, d_r=4, S=0, dtype="f32")
+    lens = np.array([12, 7])
+    inp = W.make_gva_inputs(wl, lens=lens, seed=62)
+    rng = np.random.default_rng(63)
+    nq = 12
+    qn = rng.standard_normal((2, nq, 8, 8))
+    qr = rng.standard_normal((2, nq, 8, 4))
+    got = O.gva_prefill(inp.V, inp.kr, qn, qr, inp.M, lens, 0.25)
+    for h in range(8):
+        assert np.array_equal(got[0, 0, h], inp.V[0][h // 2, 0])
+    last = O.gva_decode_seq(inp.V[0], inp.kr[0], qn[0, -1], qr[0, -1], inp.M, 12, 0.25)
+    assert np.allclose(got[0, -1], last, rtol=0, atol=1e-13)
+    # sequence 1 (7 tokens, 12 queries): the first five read nothing
+    assert np.all(got[1, :5] == 0.0) and np.all(np.abs(got[1, 5:]).sum(axis=-1) > 0)
+    const = [np.full_like(v, 0.75) for v in inp.V]
+    got_c = O.gva_prefill(const, inp.kr, qn, qr, inp.M, lens, 0.25)
+    assert np.allclose(got_c[0], 0.75, atol=1e-14) and np.allclose(got_c[1, 5:], 0.75, atol=1e-14)
+    V2 = [v.copy() for v in inp.V]
+    kr2 = [k.copy() for k in inp.kr]
+    V2[0][:, 6:] = rng.standard_normal(V2[0][:, 6:].shape)
+    kr2[0][6:] = rng.standard_normal(kr2[0][6:].shape)
+    got2 = O.gva_prefill(V2, kr2, qn, qr, inp.M, lens, 0.25)
+    assert np.array_equal(got2[0, :6], got[0, :6]) and not np.allclose(got2[0, 6:], got[0, 6:])
+
+
+def test_prefill_equals_the_per_query_decode_loop():
+    """The masked-matrix form against the per-query loop (gva_decode_multi),
+    from pre-RoPE inputs, including a sequence shorter than the query count."""
+    wl = W.Workload("pin_prefill3", 9, B=3, H=8, G=2, d_n=8, d_v=8, d_r=4, S=0, dtype="f32")
+    lens = np.array([20, 9, 1])
+    inp = W.make_gva_inputs(wl, lens=lens, seed=64)
+    rng = np.random.default_rng(65)
+    nq = 10
+    qn = rng.standard_normal((3, nq, 8, 8))
+    qr = rng.standard_normal((3, nq, 8, 4))
+    a = O.gva_prefill_step(inp.V, inp.kr, qn, qr, inp.M, lens, 0.3, 10000.0, "f32")
+    b = O.gva_decode_multi_step(inp.V, inp.kr, qn, qr, inp.M, lens, 0.3, 10000.0, "f32")
+    assert np.allclose(a, b, rtol=0, atol=1e-12)
