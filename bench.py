@@ -21,7 +21,10 @@ the same way and reported beside it.
 
 `--mode gqa` instead times gva_decode against the same-shape GQA reference
 (gva_gqa_ref_decode, K and V caches) on the wide workload and reports the
-time ratio beside the ratio of the bytes each must read.
+time ratio beside the ratio of the bytes each must read. `--mode folded`,
+`multi`, `lifecycle` and `prefill` time the maps folded into the query
+projection, several queries per sequence, the paged-cache block operations
+and the causal prefill (against the matrix-core peak).
 """
 from __future__ import annotations
 
@@ -36,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X
 METRIC = "GVA decode steps/s + effective cache-read GB/s (% HBM peak), B=16 S=4096 bf16"
 
 
@@ -58,7 +62,7 @@ def parse():
     p.add_argument("--profile-copy-mb", type=int, default=0,
                    help="with --profile-step/--profile-decode: first run a plain elementwise copy "
                         "(read N MiB, write N MiB) three times, the reference for traffic counters")
-    p.add_argument("--mode", choices=["step", "gqa", "folded", "multi", "lifecycle"], default="step")
+    p.add_argument("--mode", choices=["step", "gqa", "folded", "multi", "lifecycle", "prefill"], default="step")
     return p.parse_args()
 
 
@@ -93,6 +97,9 @@ def main():
         return
     if args.mode == "lifecycle":
         lifecycle_bench(args)
+        return
+    if args.mode == "prefill":
+        prefill_bench(args)
         return
     wl = W.WORKLOADS[args.workload]
     if args.split >= 0:
@@ -543,6 +550,81 @@ def multi_compare(args):
         res[f"nq{nq}"] = {"us": round(us, 3), "cache_GBps": round(nbytes / us / 1e3, 1),
                           "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4),
                           "query_tokens_per_s": round(wl.B * nq / us * 1e6, 1)}
+    print(json.dumps(res), flush=True)
+
+
+def prefill_flops(B: int, H: int, n: int, nq: int, d_v: int, d_r: int, d_n: int, absorb: bool) -> float:
+    """Algorithmic flops of a causal prefill: per (sequence, head, query j at
+    position n - n_q + j, cached token t <= that position) a score over the
+    absorbed key width and the positional slice (2*(d_v + d_r)) and the
+    probability-weighted value row (2*d_v); plus the absorption q' = M q
+    (2*d_n*d_v per query and head) when the maps are given."""
+    pos = [n - nq + j for j in range(nq)]
+    pairs = sum(p + 1 for p in pos if p >= 0)
+    f = B * H * pairs * (2.0 * (d_v + d_r) + 2.0 * d_v)
+    if absorb:
+        f += B * nq * H * 2.0 * d_n * d_v
+    return f
+
+
+def prefill_bench(args):
+    """`--mode prefill`: gva_prefill on the mid shape (B=16, a 4096-token
+    prompt, H=16, G=4, d_r=16), the whole prompt as queries, and the last
+    512-token chunk of a chunked prefill of the same prompt; K launches in one
+    graph, HIP events around the replay. Compute-bound: reported against the
+    dense bf16 matrix-core peak."""
+    import numpy as np
+    import torch
+
+    import compact_kv_cache_amd as gva
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS[args.workload]
+    K = args.steps
+    n = wl.S
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 9))
+    V = torch.from_numpy(rng.standard_normal((wl.B, wl.G, n, wl.d_v), dtype=np.float32)).to(dev).bfloat16()
+    Kr = torch.from_numpy(rng.standard_normal((wl.B, n, wl.d_r), dtype=np.float32)).to(dev).bfloat16()
+    M = (torch.randn(wl.H, wl.d_v, wl.d_n, device=dev) / 8).bfloat16()
+    seq = torch.full((wl.B,), n, dtype=torch.int32, device=dev)
+    shape = gva.make_shape(wl.B, wl.H, wl.G, wl.d_n, wl.d_v, wl.d_r, capacity=n, max_seq_len=n, dtype=wl.dtype)
+    res = {"mode": "prefill",
+           "config": {"workload": f"{wl.name} prefill: B={wl.B} prompt n={n} H={wl.H} G={wl.G} d_v=d_n={wl.d_v} "
+                                  f"d_r={wl.d_r} {wl.dtype}, contiguous cache, maps M in the kernel",
+                      "steps": K}}
+    for label, nq in (("full_prompt", n), ("last_chunk_512", 512)):
+        q = torch.randn(wl.B, nq, wl.H, wl.d_n, device=dev).bfloat16()
+        qr = torch.randn(wl.B, nq, wl.H, wl.d_r, device=dev).bfloat16()
+        out = torch.empty(wl.B, nq, wl.H, wl.d_v, dtype=torch.bfloat16, device=dev)
+
+        def call():
+            gva.gva_prefill(shape, nq, q, qr, M, V, Kr, seq, None, wl.scale, out)
+
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(K):
+                call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / K * 1e3
+        fl = prefill_flops(wl.B, wl.H, n, nq, wl.d_v, wl.d_r, wl.d_n, True)
+        tf = fl / us / 1e6
+        res[label] = {"n_q": nq, "us": round(us, 2), "flops": fl, "TFLOPs": round(tf, 1),
+                      "frac_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "query_tokens_per_s": round(wl.B * nq / us * 1e6, 1)}
+        del q, qr, out, g
+    full = res["full_prompt"]
+    res["roofline"] = {"bound": "mfma", "achieved": full["TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": full["frac_bf16_peak"], "traffic": None,
+                       "kernel": "prefill_mfma_kernel (whole prompt)"}
     print(json.dumps(res), flush=True)
 
 
