@@ -11,15 +11,17 @@
 // One staged tile of V_g and k_r feeds every head of the group and every
 // query of the workgroup.
 //
-// Work split: one workgroup of 8 waves per (sequence, group, block of
+// Work split: one workgroup of 4 waves per (sequence, group, block of
 // 16 * 16 / (H/G) queries). The block's (query, head) pairs form 16 blocks of
-// 16 matrix-core columns (16 queries of one head each); every wave owns two
+// 16 matrix-core columns (16 queries of one head each); every wave owns four
 // column blocks and keeps their absorbed queries, running softmax state and
-// output accumulators in registers. The workgroup walks the key tiles
-// 0 .. (last query's position) / 64 once: each tile is loaded by all 512
-// threads (one 16-byte buffer load each for the V rows, the positional keys
+// output accumulators in registers (≈ 250 VGPRs: two waves per SIMD, two
+// workgroups per compute unit). The workgroup walks the key tiles
+// 0 .. (last query's position) / 64 once: each tile is loaded by its 256
+// threads (two 16-byte buffer loads each for the V rows, the positional keys
 // alongside), stored to one of two LDS buffers while the previous one is
-// computed, and read by every wave. Per wave and tile, on
+// computed, and read by every wave. (Measured at the mid shape: 4 waves x 4
+// blocks ran 1.29x faster than 8 waves x 2 blocks.) Per wave and tile, on
 // v_mfma_f32_16x16x32_bf16:
 //   scores  S^T[tok][col] = V[tok] . q'[col] + k_r[tok] . q_rope[col] (A = V
 //           rows from LDS, B = the column block's queries), 12 MFMAs per block;
@@ -39,8 +41,8 @@
 namespace gva {
 namespace {
 
-constexpr int kPWaves = 8;           // waves per workgroup
-constexpr int kCB = 2;               // 16-column blocks per wave
+constexpr int kPWaves = 4;           // waves per workgroup
+constexpr int kCB = 4;               // 16-column blocks per wave
 constexpr float kRescaleLog2P = 8.f; // move the reference max only beyond 2^8
 
 template <int HPG>
@@ -100,7 +102,8 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
     if (a.M != nullptr) {  // uniform
       // q'^T = M_h q^T: A = rows of M_h in the permuted order that lands the
       // product in the B layout (lane (col, r) gets q'[32*kc + 8r + e] in
-      // D[2kc + e/4][e%4]); accumulated in fp32, rounded to bf16 once.
+      // D[2kc + e/4][e%4]); accumulated in fp32, scaled by scale*log2(e) and
+      // rounded to bf16 once.
       const __bf16* Mh = reinterpret_cast<const __bf16*>(a.M) + (int64_t)h * kD * kD;
       f32x4 D[4];
 #pragma unroll
@@ -115,13 +118,18 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qb[u][kc].h[e] = (__bf16)D[2 * kc + (e >> 2)][e & 3];
+        for (int e = 0; e < 8; ++e) qb[u][kc].h[e] = (__bf16)(D[2 * kc + (e >> 2)][e & 3] * sl2);
     } else {  // q_nope already holds q' (the maps folded into the projection)
-      qb[u][0] = q_in[0];
-      qb[u][1] = q_in[1];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qb[u][kc].h[e] = (__bf16)((float)q_in[kc].h[e] * sl2);
     }
     if constexpr (DR) {
-      qr[u].u = ld16(qrp + qrow * d_r, kr_off);
+      Frag x;
+      x.u = ld16(qrp + qrow * d_r, kr_off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qr[u].h[e] = (__bf16)((float)x.h[e] * sl2);
       if (8 * r >= d_r) qr[u].u = u32x4{0u, 0u, 0u, 0u};
     }
     if (!jv) {
@@ -134,15 +142,23 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
   // their 16-byte chunks XOR-swizzled per row, then the positional-key rows.
   constexpr int kStage = 8192 + 1024 * (KR > 0 ? KR : 0);
   __shared__ __attribute__((aligned(16))) char stage[2][kStage];
-  const int vrow = tid >> 3, vch = tid & 7;  // V: thread t loads row t/8, chunk t%8
-  const int v_lds = vrow * (kD * 2) + 16 * (vch ^ stage_swizzle(vrow));
+  // V: 16-byte chunk c = t + 64*kPWaves*i of the tile (row c/8, chunk c%8)
+  constexpr int kNV = 512 / (64 * kPWaves);  // V chunks per thread
+  const int vch = tid & 7;
+  int v_lds[kNV];
+#pragma unroll
+  for (int i = 0; i < kNV; ++i) {
+    const int vrow = (tid >> 3) + 8 * kPWaves * i;
+    v_lds[i] = vrow * (kD * 2) + 16 * (vch ^ stage_swizzle(vrow));
+  }
   const __bf16* vc = reinterpret_cast<const __bf16*>(a.v_cache);
   const __bf16* krc = reinterpret_cast<const __bf16*>(a.kr_cache);
   // Tile k's rows [64k, min(64k + 64, n)) form the buffer range; rows past it,
   // a missing page and a tile past the last read as zeros without a memory
   // access. The positional keys take 64*KR threads (1 KB each per 64); the
   // other threads re-read the tile's first 16 bytes and store nothing.
-  auto load_tile = [&](int k, u32x4& rv, u32x4& rk) {
+  static_assert(64 * 4 <= 64 * kPWaves, "one positional-key chunk per thread at d_r <= 32");
+  auto load_tile = [&](int k, u32x4 (&rv)[kNV], u32x4& rk) {
     const int t0 = k * kTile;
     int rows = k < n_tiles ? min(kTile, n - t0) : 0;
     int64_t vbase = 0, kbase = 0;
@@ -157,14 +173,17 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
       kbase = rows > 0 ? ((int64_t)b * a.capacity + t0) * d_r : 0;
     }
     const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(vc + vbase), 0, rows * kD * 2, kBufferWord3);
-    rv = __builtin_amdgcn_raw_buffer_load_b128(rs, vrow * (kD * 2) + 16 * vch, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kNV; ++i)
+      rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + 64 * kPWaves * i) * 16, 0, 0);
     if constexpr (DR) {
       const auto rk_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(krc + kbase), 0, rows * 16 * KR, kBufferWord3);
       rk = __builtin_amdgcn_raw_buffer_load_b128(rk_, tid < 64 * KR ? 16 * tid : 0, 0, 0);
     }
   };
-  auto store_tile = [&](int buf, const u32x4& rv, const u32x4& rk) {
-    *reinterpret_cast<u32x4*>(&stage[buf][v_lds]) = rv;
+  auto store_tile = [&](int buf, const u32x4 (&rv)[kNV], const u32x4& rk) {
+#pragma unroll
+    for (int i = 0; i < kNV; ++i) *reinterpret_cast<u32x4*>(&stage[buf][v_lds[i]]) = rv[i];
     if constexpr (DR) {
       if (tid < 64 * KR) *reinterpret_cast<u32x4*>(&stage[buf][8192 + 16 * tid]) = rk;
     }
@@ -184,6 +203,11 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
     }
   }
 
+  // Scores come out of the matrix cores in log2 units (the queries carry
+  // scale*log2(e)) and already shifted by the column's reference max m_ref
+  // (the accumulator starts at -m_ref), so p = 2^s with no further
+  // arithmetic. m_ref is set by the column's first tile and moves only when
+  // a tile's shifted max exceeds 2^8; p stays below 256.
   f32x4 acc[kCB][4];
   float m_ref[kCB], l_run[kCB];
 #pragma unroll
@@ -193,7 +217,6 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
     m_ref[u] = -INFINITY;
     l_run[u] = 0.f;
   }
-  const float thr = kRescaleLog2P / sl2;
 
   auto compute = [&](const char* st_base, int t0) {
     if (t0 > wave_pmax) return;  // every query of the wave is before this tile (uniform)
@@ -212,7 +235,8 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
       f32x4 s[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        f32x4 c = mma(sa[st][0], qb[u][0], kZero4);
+        const float c0 = m_ref[u] == -INFINITY ? 0.f : -m_ref[u];
+        f32x4 c = mma(sa[st][0], qb[u][0], f32x4{c0, c0, c0, c0});
         c = mma(sa[st][1], qb[u][1], c);
         if constexpr (DR) c = mma(kr[st], qr[u], c);
         s[st] = c;
@@ -231,21 +255,25 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[st][i]);
       mx = rows_max(mx);
-      const float m_new = (mx > m_ref[u] + thr) ? mx : m_ref[u];
-      if (__any(m_new != m_ref[u])) {
-        const float alpha = (m_new == m_ref[u]) ? 1.f : __builtin_amdgcn_exp2f((m_ref[u] - m_new) * sl2);
+      // shift of the reference: the whole max on a column's first tile,
+      // else only beyond 2^8; none for a column whose scores are all masked
+      const bool unset = m_ref[u] == -INFINITY;
+      const float shift = (mx == -INFINITY) ? 0.f : (unset || mx > kRescaleLog2P) ? mx : 0.f;
+      if (__any(shift != 0.f)) {
+        const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-shift);  // unset: nothing accumulated
         l_run[u] *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db) acc[u][db] *= alpha;
-        m_ref[u] = m_new;
+        m_ref[u] = unset ? (mx == -INFINITY ? m_ref[u] : mx) : m_ref[u] + shift;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) s[st] -= shift;
       }
-      const float bias = (m_ref[u] == -INFINITY) ? 0.f : -m_ref[u] * sl2;
       float psum = 0.f;
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s[st][i] = __builtin_amdgcn_exp2f(fmaf(s[st][i], sl2, bias));
+          s[st][i] = __builtin_amdgcn_exp2f(s[st][i]);
           psum += s[st][i];
         }
       l_run[u] += psum;
@@ -275,7 +303,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
       }
   };
 
-  u32x4 rv = u32x4{0u, 0u, 0u, 0u}, rk = u32x4{0u, 0u, 0u, 0u};
+  u32x4 rv[kNV], rk = u32x4{0u, 0u, 0u, 0u};
   load_tile(0, rv, rk);
   store_tile(0, rv, rk);
   __syncthreads();
