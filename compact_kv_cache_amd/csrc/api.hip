@@ -279,7 +279,7 @@ gva_status gva_prefill(const gva_shape* shape, int32_t n_q, const void* q_nope, 
   a.max_blocks = shape->max_blocks_per_seq;
   a.max_seq_len = shape->max_seq_len;
   a.nq = n_q;
-  const int qw = gva::prefill_queries_per_block(shape->H / shape->G);
+  const int qw = gva::prefill_queries_per_block(shape->H / shape->G, shape->d_r);
   a.n_qblk = (n_q + qw - 1) / qw;
   a.q_nope = q_nope;
   a.q_rope = q_rope;

@@ -182,6 +182,6 @@ hipError_t launch_decode_mfma(const DecodeLaunch& a, hipStream_t s);  // bf16 on
 hipError_t launch_gqa_mfma(const DecodeLaunch& a, hipStream_t s);     // bf16 only
 hipError_t launch_step_mfma(const DecodeLaunch& a, hipStream_t s);    // bf16 only, a.step set
 hipError_t launch_prefill_mfma(const PrefillLaunch& a, hipStream_t s);
-int prefill_queries_per_block(int hpg);  // queries per workgroup of the prefill kernel
+int prefill_queries_per_block(int hpg, int d_r);  // queries per workgroup of the prefill kernel
 
 }  // namespace gva

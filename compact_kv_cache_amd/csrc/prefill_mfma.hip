@@ -12,24 +12,25 @@
 // query of the workgroup.
 //
 // Work split: one workgroup of 4 waves per (sequence, group, block of
-// 16 * 16 / (H/G) queries). The block's (query, head) pairs form 16 blocks of
-// 16 matrix-core columns (16 queries of one head each); every wave owns four
-// column blocks and keeps their absorbed queries, running softmax state and
-// output accumulators in registers (≈ 250 VGPRs: two waves per SIMD, two
-// workgroups per compute unit). The workgroup walks the key tiles
-// 0 .. (last query's position) / 64 once: each tile is loaded by its 256
-// threads (two 16-byte buffer loads each for the V rows, the positional keys
-// alongside), stored to one of two LDS buffers while the previous one is
-// computed, and read by every wave. (Measured at the mid shape: 4 waves x 4
-// blocks ran 1.29x faster than 8 waves x 2 blocks.) Per wave and tile, on
-// v_mfma_f32_16x16x32_bf16:
+// queries). The block's (query, head) pairs form blocks of 16 matrix-core
+// columns (16 queries of one head each); every wave owns four column blocks
+// (three where four would not fit 256 registers without spilling: H/G < 4 or
+// d_r = 32) and keeps their absorbed queries, running softmax state and
+// output accumulators in registers (two waves per SIMD, two workgroups per
+// compute unit). The workgroup walks the key tiles 0 .. (last query's
+// position) / 64 once: each tile is loaded by its 256 threads (two 16-byte
+// buffer loads each for the V rows, the positional keys alongside), stored
+// to one of two LDS buffers while the other is computed, and read by every
+// wave. (Measured at the mid shape: 4 waves x 4 blocks ran 1.29x faster than
+// 8 waves x 2 blocks.) Per wave and tile, on the matrix cores:
 //   scores  S^T[tok][col] = V[tok] . q'[col] + k_r[tok] . q_rope[col] (A = V
-//           rows from LDS, B = the column block's queries), 12 MFMAs per block;
+//           rows from LDS, B = the column block's queries), 8 MFMAs of
+//           16x16x32 per block, and 4 of 16x16x16 for d_r <= 16 (else 16x16x32);
 //   mask    tokens past a column's own position (tiles on the diagonal only);
 //   softmax online per column, the max over the wave's four 16-lane rows with
 //           the row-swap permutes;
 //   P.V     O^T[ch][col] += V^T[ch][tok] . P^T[tok][col], A = V^T from the
-//           LDS transpose load (shared by both column blocks), B = the score
+//           LDS transpose load (shared by the wave's column blocks), B = the score
 //           accumulator in bf16, 8 MFMAs per block.
 // Workgroup ids put all query blocks of one (sequence, group) on one XCD, so
 // the tiles that every block re-reads come from that XCD's L2, and the
@@ -42,18 +43,35 @@ namespace gva {
 namespace {
 
 constexpr int kPWaves = 4;           // waves per workgroup
-constexpr int kCB = 4;               // 16-column blocks per wave
 constexpr float kRescaleLog2P = 8.f; // move the reference max only beyond 2^8
 
-template <int HPG>
+// 4-element operand of v_mfma_f32_16x16x16_bf16 (lane: row or column
+// lane%16, k = 4*(lane/16) .. +3)
+union Frag4 {
+  i16x4 s;
+  uint2 u;
+  __bf16 h[4];
+};
+__device__ __forceinline__ f32x4 mma16(const Frag4& a, const Frag4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.s, b.s, c, 0, 0, 0);
+}
+
+// 16-column blocks per wave: 4 where the state fits the 256 registers of a
+// wave at two waves per SIMD without spilling, else 3.
+template <int HPG, int KR>
+constexpr int prefill_column_blocks() {
+  return (HPG == 4 && KR <= 3) || (HPG == 2 && KR == 3) || KR == 0 ? 4 : 3;
+}
+template <int HPG, int KR>
 constexpr int prefill_queries_per_block() {
-  return 16 * kCB * kPWaves / HPG;
+  return 16 * prefill_column_blocks<HPG, KR>() * kPWaves / HPG;
 }
 
 template <int HPG, bool PAGED, int KR>
 __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLaunch a) {
   constexpr bool DR = KR > 0;  // positional slice present (d_r = 8 * KR)
-  constexpr int QW = prefill_queries_per_block<HPG>();
+  constexpr int kCB = prefill_column_blocks<HPG, KR>();
+  constexpr int QW = prefill_queries_per_block<HPG, KR>();
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, r = lane >> 4;
@@ -80,8 +98,11 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
   // ---- the wave's column blocks: absorbed queries as B operands ---------------
   const __bf16* qn = reinterpret_cast<const __bf16*>(a.q_nope);
   const __bf16* qrp = reinterpret_cast<const __bf16*>(a.q_rope);
-  Frag qb[kCB][2], qr[kCB];
-  int pcol[kCB];                 // position of this lane's column query (-1: none)
+  // Positional slice: d_r <= 16 fits one K = 16 product (4 channels per
+  // lane), wider slices take the K = 32 product like the content part.
+  constexpr bool K16 = DR && KR <= 2;
+  Frag qb[kCB][2], qr[K16 ? 1 : kCB];
+  Frag4 qr4[K16 ? kCB : 1];
   int wave_pmin = INT32_MAX, wave_pmax = -1;  // over the wave's columns (uniform)
 #pragma unroll
   for (int u = 0; u < kCB; ++u) {
@@ -89,7 +110,6 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
     const int h = g * HPG + jh;
     const int j = q0 + 16 * qg + col;
     const bool jv = j < nq && first + j >= 0;
-    pcol[u] = jv ? first + j : -1;
     const int j_lo = q0 + 16 * qg, j_hi = min(q0 + 16 * qg + 15, nq - 1);
     if (j_lo <= j_hi) {
       wave_pmin = min(wave_pmin, first + j_lo);
@@ -125,7 +145,13 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
 #pragma unroll
         for (int e = 0; e < 8; ++e) qb[u][kc].h[e] = (__bf16)((float)q_in[kc].h[e] * sl2);
     }
-    if constexpr (DR) {
+    if constexpr (K16) {
+      Frag4 x;
+      x.u = *reinterpret_cast<const uint2*>(qrp + qrow * d_r + 4 * min(r, 2 * KR - 1));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qr4[u].h[e] = (__bf16)((float)x.h[e] * sl2);
+      if (4 * r >= d_r || !jv) qr4[u].u = uint2{0u, 0u};
+    } else if constexpr (DR) {
       Frag x;
       x.u = ld16(qrp + qrow * d_r, kr_off);
 #pragma unroll
@@ -133,7 +159,8 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
       if (8 * r >= d_r) qr[u].u = u32x4{0u, 0u, 0u, 0u};
     }
     if (!jv) {
-      qb[u][0].u = qb[u][1].u = qr[u].u = u32x4{0u, 0u, 0u, 0u};
+      qb[u][0].u = qb[u][1].u = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (!K16) qr[u].u = u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -193,14 +220,13 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
   // V^T through the LDS transpose load: lane j of a 16-lane group r addresses
   // staged token 4r + j/4 (+ 16h + 32pr) and channels 16db + 4(j%4) .. +3;
   // lane col receives channel 16db + col of four consecutive tokens.
-  int tr_off[4];
+  // Channel block db only flips bits 5-6 of the offset: chunk 2db + (col%4)/2
+  // XOR the row swizzle is (2db) ^ ((col%4)/2 ^ swizzle), so offset(db) =
+  // offset(0) ^ 32db.
+  int tr_off0;
   {
     const int row = 4 * r + (col >> 2);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int chan = 16 * db + 4 * (col & 3);
-      tr_off[db] = row * (kD * 2) + 16 * ((chan >> 3) ^ stage_swizzle(row)) + 2 * (chan & 7);
-    }
+    tr_off0 = row * (kD * 2) + 16 * (((col & 3) >> 1) ^ stage_swizzle(row)) + 8 * (col & 1);
   }
 
   // Scores come out of the matrix cores in log2 units (the queries carry
@@ -220,14 +246,18 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
 
   auto compute = [&](const char* st_base, int t0) {
     if (t0 > wave_pmax) return;  // every query of the wave is before this tile (uniform)
-    Frag sa[4][2], kr[4];
+    Frag sa[4][2], kr[K16 ? 1 : 4];
+    Frag4 kr4[K16 ? 4 : 1];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int row = 16 * st + col;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
         sa[st][hh].u = *reinterpret_cast<const u32x4*>(st_base + row * (kD * 2) + 16 * ((4 * hh + r) ^ stage_swizzle(row)));
-      if constexpr (DR) kr[st].u = *reinterpret_cast<const u32x4*>(st_base + 8192 + row * (16 * KR) + 2 * kr_off);
+      if constexpr (K16)
+        kr4[st].u = *reinterpret_cast<const uint2*>(st_base + 8192 + row * (16 * KR) + 8 * min(r, 2 * KR - 1));
+      else if constexpr (DR)
+        kr[st].u = *reinterpret_cast<const u32x4*>(st_base + 8192 + row * (16 * KR) + 2 * kr_off);
     }
     Frag pb[kCB][2];
 #pragma unroll
@@ -238,16 +268,22 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
         const float c0 = m_ref[u] == -INFINITY ? 0.f : -m_ref[u];
         f32x4 c = mma(sa[st][0], qb[u][0], f32x4{c0, c0, c0, c0});
         c = mma(sa[st][1], qb[u][1], c);
-        if constexpr (DR) c = mma(kr[st], qr[u], c);
+        if constexpr (K16)  // own accumulator: chained after (or before) the K = 32 products
+          c += mma16(kr4[st], qr4[u], kZero4);  // through one accumulator it gave wrong sums
+        else if constexpr (DR)
+          c = mma(kr[st], qr[u], c);
         s[st] = c;
       }
       // causal mask on the diagonal tiles: token past the column's position
       if (t0 + kTile - 1 > wave_pmin) {
+        // position of this lane's column query (-1: no query, nothing visible)
+        const int jq = q0 + 16 * ((kCB * w + u) / HPG) + col;
+        const int pcol = (jq < nq && first + jq >= 0) ? first + jq : -1;
 #pragma unroll
         for (int st = 0; st < 4; ++st)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (t0 + 16 * st + 4 * r + i > pcol[u]) s[st][i] = -INFINITY;
+            if (t0 + 16 * st + 4 * r + i > pcol) s[st][i] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -293,7 +329,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const i16x4 xv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(st_base + tr_off[db] + (32 * pr + 16 * hh) * (kD * 2)));
+              (lds_i16x4*)(st_base + (tr_off0 ^ (32 * db)) + (32 * pr + 16 * hh) * (kD * 2)));
           const uint2 xb = __builtin_bit_cast(uint2, xv);
           vt.u[2 * hh] = xb.x;
           vt.u[2 * hh + 1] = xb.y;
@@ -363,9 +399,20 @@ hipError_t prefill_dr(const PrefillLaunch& a, hipStream_t s) {
 
 }  // namespace
 
-int prefill_queries_per_block(int hpg) {
-  return hpg == 1 ? prefill_queries_per_block<1>() : hpg == 2 ? prefill_queries_per_block<2>()
-                                                               : prefill_queries_per_block<4>();
+template <int HPG>
+int queries_per_block_dr(int d_r) {
+  switch (d_r / 8) {
+    case 0: return prefill_queries_per_block<HPG, 0>();
+    case 1: return prefill_queries_per_block<HPG, 1>();
+    case 2: return prefill_queries_per_block<HPG, 2>();
+    case 3: return prefill_queries_per_block<HPG, 3>();
+    default: return prefill_queries_per_block<HPG, 4>();
+  }
+}
+
+int prefill_queries_per_block(int hpg, int d_r) {
+  return hpg == 1 ? queries_per_block_dr<1>(d_r) : hpg == 2 ? queries_per_block_dr<2>(d_r)
+                                                             : queries_per_block_dr<4>(d_r);
 }
 
 hipError_t launch_prefill_mfma(const PrefillLaunch& a, hipStream_t s) {
