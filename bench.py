@@ -601,9 +601,12 @@ def prefill_bench(args):
         def call():
             gva.gva_prefill(shape, nq, q, qr, M, V, Kr, seq, None, wl.scale, out)
 
-        for _ in range(3):
-            call()
-        torch.cuda.synchronize()
+        # warm-up long enough (about half a second) for the clocks to settle
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < 0.5:
+            for _ in range(5):
+                call()
+            torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(K):
