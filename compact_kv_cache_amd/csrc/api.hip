@@ -8,6 +8,7 @@
 
 #include "../../include/gva.h"
 #include "launch.hpp"
+#include "prefill.hpp"
 
 namespace {
 

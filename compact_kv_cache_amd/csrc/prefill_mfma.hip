@@ -37,6 +37,7 @@
 // latest (longest) query blocks are dispatched first.
 #include "gva_device.hpp"
 #include "launch.hpp"
+#include "prefill.hpp"
 #include "mfma_common.hpp"
 
 namespace gva {
