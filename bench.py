@@ -22,9 +22,10 @@ the same way and reported beside it.
 `--mode gqa` instead times gva_decode against the same-shape GQA reference
 (gva_gqa_ref_decode, K and V caches) on the wide workload and reports the
 time ratio beside the ratio of the bytes each must read. `--mode folded`,
-`multi`, `lifecycle` and `prefill` time the maps folded into the query
-projection, several queries per sequence, the paged-cache block operations
-and the causal prefill (against the matrix-core peak).
+`multi`, `lifecycle`, `prefill` and `ragged` time the maps folded into the
+query projection, several queries per sequence, the paged-cache block
+operations, the causal prefill (against the matrix-core peak) and the ragged
+paged batch.
 """
 from __future__ import annotations
 
@@ -62,7 +63,8 @@ def parse():
     p.add_argument("--profile-copy-mb", type=int, default=0,
                    help="with --profile-step/--profile-decode: first run a plain elementwise copy "
                         "(read N MiB, write N MiB) three times, the reference for traffic counters")
-    p.add_argument("--mode", choices=["step", "gqa", "folded", "multi", "lifecycle", "prefill"], default="step")
+    p.add_argument("--mode", choices=["step", "gqa", "folded", "multi", "lifecycle", "prefill", "ragged"],
+                   default="step")
     return p.parse_args()
 
 
@@ -100,6 +102,9 @@ def main():
         return
     if args.mode == "prefill":
         prefill_bench(args)
+        return
+    if args.mode == "ragged":
+        ragged_bench(args)
         return
     wl = W.WORKLOADS[args.workload]
     if args.split >= 0:
@@ -629,6 +634,86 @@ def prefill_bench(args):
     res["roofline"] = {"bound": "mfma", "achieved": full["TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS,
                        "unit": "TFLOP/s", "frac": full["frac_bf16_peak"], "traffic": None,
                        "kernel": "prefill_mfma_kernel (whole prompt)"}
+    print(json.dumps(res), flush=True)
+
+
+def ragged_bench(args):
+    """`--mode ragged`: the ragged paged workload (B=64, lengths uniform in
+    [1024, 32768] from the workload's seed, 64-token blocks in a shuffled
+    table): gva_decode and the fused step (one appended token per sequence),
+    K launches in one graph over R cold replicas of the page pool."""
+    import numpy as np
+    import torch
+
+    import compact_kv_cache_amd as gva
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS["ragged_paged"]
+    K = args.steps
+    lens = W.ragged_lens(wl)
+    extra = K + 8
+    table, nblk = W.paged_pool(lens + extra, 64, wl.seed)
+    bpt = gva.gva_cache_bytes_per_token(wl.G, wl.d_v, wl.d_r, wl.dtype)
+    pool_bytes = nblk * 64 * bpt
+    R = max(2, math.ceil(512e6 / pool_bytes))
+    reps = []
+    for _ in range(R):
+        v = torch.randn(nblk, wl.G, 64, wl.d_v, device=dev).bfloat16()
+        k = torch.randn(nblk, 64, wl.d_r, device=dev).bfloat16()
+        reps.append((v, k, (torch.randn(wl.H, wl.d_v, wl.d_n, device=dev) / 8).bfloat16(),
+                     torch.tensor(lens.astype(np.int32), device=dev)))
+    tab = torch.tensor(table, device=dev)
+    q = torch.randn(wl.B, wl.H, wl.d_n, device=dev).bfloat16()
+    qr = torch.randn(wl.B, wl.H, wl.d_r, device=dev).bfloat16()
+    out = torch.empty(wl.B, wl.H, wl.d_v, dtype=torch.bfloat16, device=dev)
+    v_new = torch.randn(wl.B, wl.G, wl.d_v, device=dev).bfloat16()
+    k_new = torch.randn(wl.B, wl.d_r, device=dev).bfloat16()
+    n_max = int(lens.max()) + extra
+
+    def shape_at(n):
+        return gva.make_shape(wl.B, wl.H, wl.G, wl.d_n, wl.d_v, wl.d_r, max_seq_len=n, block_size=64,
+                              num_blocks=nblk, max_blocks_per_seq=table.shape[1],
+                              split_tokens=max(args.split, 0), dtype=wl.dtype)
+
+    shape = shape_at(n_max)
+    ws = torch.zeros(gva.gva_decode_step_workspace_bytes(shape) // 4 + 1, device=dev)
+
+    def dec(i):
+        v, k, M, sl = reps[i % R]
+        gva.gva_decode(shape, q, qr, M, v, k, sl, tab, wl.scale, out, ws)
+
+    def step(i):
+        v, k, M, sl = reps[i % R]
+        gva.gva_decode_step(shape, v_new, k_new, q, qr, M, v, k, sl, tab, wl.scale, wl.rope_base, out, ws)
+
+    res = {"mode": "ragged",
+           "config": {"workload": f"ragged_paged: B={wl.B} lengths U[{wl.len_lo}, {wl.len_hi}] (seeded, "
+                                  f"mean {lens.mean():.0f}) H={wl.H} G={wl.G} d_r={wl.d_r} bf16, 64-token pages "
+                                  f"in a shuffled table, {R} cold replicas of the page pool", "steps": K,
+                      "split_tokens": gva.gva_decode_split_tokens(shape_at(n_max))}}
+    for label, fn in (("decode", dec), ("fused_step", step)):
+        for i in range(2 * R):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                fn(i)
+        torch.cuda.synchronize()
+        before = sum(int(r[3].sum()) for r in reps)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / K * 1e3
+        # cache tokens read per launch: every replica's current lengths (the step reads its new token too)
+        after = sum(int(r[3].sum()) for r in reps)
+        tokens = (before + after) / 2 / R if label == "fused_step" else before / R
+        nbytes = tokens * bpt
+        res[label] = {"us": round(us, 2), "cache_bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+                      "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
     print(json.dumps(res), flush=True)
 
 

@@ -123,6 +123,13 @@ class GvaInputs:
     M: np.ndarray
 
 
+def ragged_lens(wl: Workload, seed: Optional[int] = None) -> np.ndarray:
+    """The ragged workload's sequence lengths: the first draw of the
+    workload's generator, exactly as make_gva_inputs draws them."""
+    rng = np.random.Generator(np.random.PCG64(wl.seed if seed is None else seed))
+    return rng.integers(wl.len_lo, wl.len_hi, size=wl.B, endpoint=True)
+
+
 def make_gva_inputs(wl: Workload, extra: int = 0, seed: Optional[int] = None,
                     lens: Optional[np.ndarray] = None) -> GvaInputs:
     """Draw one seeded problem. `extra` = tokens reserved for later appends."""
