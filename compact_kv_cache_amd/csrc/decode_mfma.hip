@@ -399,11 +399,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     }
   }
   __syncthreads();
-  // The second tile of every wave is requested only now: issued with the
-  // first it would hold this barrier (a wave stalls at load issue while the
-  // compute unit's request queue is full).
-  Tile<GQA, KR> Y;
-  issue(Y, w + kWaves, t_end, n_tiles);
   // absorbed query as the bf16 B operand (accumulated in fp32, rounded once)
   Frag qb[2];
 #pragma unroll
@@ -567,25 +562,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     }
   };
 
-  // Each tile is staged, its registers are reloaded at once with the tile
-  // two rounds ahead, and the math runs on the staged copy.
-  // The loop has a single exit and issues both reloads on every path (a
-  // reload past the last tile has an empty range: zeros, no memory access),
-  // so the compiler's wait counts for each tile stay exact across iterations.
+  // Each tile is staged, its registers are reloaded at once with the wave's
+  // next tile, and the math runs on the staged copy: one tile in flight per
+  // wave while it computes. (Eight waves of one compute unit then keep about
+  // 80 KB of reads in flight, more than the rate needs. A second tile in
+  // flight made a wave stall at load issue while the unit's request queue was
+  // full, with a staged tile waiting behind the stalled instruction.)
+  // The loop has a single exit and issues the reload on every path (a reload
+  // past the last tile has an empty range: zeros, no memory access), so the
+  // compiler's wait count for each tile stays exact across iterations.
   Frags<DR> F;
 #pragma clang loop unroll(disable)
-  for (int k = w; k < n_tiles; k += 2 * kWaves) {
+  for (int k = w; k < n_tiles; k += kWaves) {
     stage(X);
     fragments(F, X);
-    issue(X, k + 2 * kWaves, t_end, n_tiles);
+    issue(X, k + kWaves, t_end, n_tiles);
     process(F);
-    const bool has_y = k + kWaves < n_tiles;  // wave-uniform
-    if (has_y) {
-      stage(Y);
-      fragments(F, Y);
-    }
-    issue(Y, k + 3 * kWaves, t_end, n_tiles);
-    if (has_y) process(F);
   }
 
   // ---- merge the waves ----------------------------------------------------------------
