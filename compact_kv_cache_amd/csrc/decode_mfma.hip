@@ -105,13 +105,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   const int col = lane & 15, r = lane >> 4;                 // MFMA column / lane group
   const int H = a.H, G = a.G, d_r = a.d_r;
 
-  // Fused step: waves 4..7 rotate the group's query slices (pairs
+  // Fused step: the first waves rotate the group's query slices (pairs
   // 0 .. HPG*d_r/2-1) and the appended key (the next d_r/2 pairs), exactly as
-  // gva_rope_query and gva_append do.
+  // gva_rope_query and gva_append do, lane i of the workgroup taking pair i.
+  // (Waves 0..3 get their load instructions through first and reach the
+  // query barrier about a microsecond before waves 4..7, so the rotation
+  // there stays off the barrier's path.)
   constexpr int half = 4 * (KR > 0 ? KR : 1);  // rotation pairs per row (d_r / 2)
-  const int rot_i = (w - 4) * 64 + lane;  // pair handled by this lane (waves 4..7)
-  const bool rot_q = STEP && DR && w >= 4 && rot_i < HPG * half;
-  const bool rot_k = STEP && DR && w >= 4 && !rot_q && rot_i < HPG * half + half;
+  const int rot_i = w * 64 + lane;  // pair handled by this lane
+  const bool rot_q = STEP && DR && w < 4 && rot_i < HPG * half;
+  const bool rot_k = STEP && DR && w < 4 && !rot_q && rot_i < HPG * half + half;
   const int rot_j = rot_q ? rot_i / half : 0;  // head within the group
   const int rot_p = rot_q ? rot_i % half : (rot_k ? rot_i - HPG * half : 0);  // pair index
 
@@ -568,15 +571,15 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   // 80 KB of reads in flight, more than the rate needs. A second tile in
   // flight made a wave stall at load issue while the unit's request queue was
   // full, with a staged tile waiting behind the stalled instruction.)
-  // The loop has a single exit and issues the reload on every path (a reload
-  // past the last tile has an empty range: zeros, no memory access), so the
-  // compiler's wait count for each tile stays exact across iterations.
+  // With one tile in flight the wait before staging covers every outstanding
+  // load on any path, so the reload is simply skipped after the wave's last
+  // tile (an empty-range load would still take a slot in the request queue).
   Frags<DR> F;
 #pragma clang loop unroll(disable)
   for (int k = w; k < n_tiles; k += kWaves) {
     stage(X);
     fragments(F, X);
-    issue(X, k + kWaves, t_end, n_tiles);
+    if (k + kWaves < n_tiles) issue(X, k + kWaves, t_end, n_tiles);  // wave-uniform
     process(F);
   }
 
