@@ -82,6 +82,37 @@ def test_step_equals_three_calls(dtype, paged, split):
     assert torch.equal(qr, S.dev(inp.q_rope, dtype)), "q_rope must not be modified"
 
 
+@pytest.mark.parametrize("hpg,d_r", [(4, 8), (4, 24), (4, 32), (1, 16), (2, 16), (2, 24)])
+def test_step_positional_widths_and_head_groups(hpg, d_r):
+    """Fused step at the other positional widths (the rotation spans one or
+    two waves of the workgroup) and heads per group: bit-for-bit equal to the
+    three calls, and within tolerance of the oracle's step."""
+    wl = W.Workload("step_shapes", 9, B=3, H=4 * hpg, G=4, d_n=64, d_v=64, d_r=d_r, S=0, dtype="bf16")
+    lens = np.array([300, 77, 700])
+    cap = 800
+    inp, (ca, cb) = _pair_of_caches(wl, lens, cap, False, seed=11 + d_r + hpg)
+    qn, qr, Md = (S.dev(x, "bf16") for x in (inp.q_nope, inp.q_rope, inp.M))
+    out_a = torch.empty(wl.B, wl.H, 64, dtype=torch.bfloat16, device="cuda")
+    out_b = torch.empty_like(out_a)
+    q_rot = torch.empty_like(qr)
+    ws_b = cb.step_workspace(int(lens.max()) + 3, 256)
+    for i in range(2):
+        max_len = int(lens.max()) + i + 1
+        print(f"[case] step hpg={hpg} d_r={d_r} i={i}", flush=True)
+        v1, k1 = _new_token(inp, lens, i, "bf16")
+        ca.append(v1.unsqueeze(2).contiguous(), k1.unsqueeze(1).contiguous(), BASE)
+        gva.gva_rope_query(ca.shape(max_len, 256), qr, q_rot, ca.seq_lens, BASE)
+        ca.decode(qn, q_rot, Md, wl.scale, out_a, max_len, 256)
+        cb.step(v1, k1, qn, qr, Md, wl.scale, out_b, max_len, 256, workspace=ws_b)
+        torch.cuda.synchronize()
+        assert torch.equal(ca.seq_lens, cb.seq_lens)
+        assert torch.equal(out_a, out_b), (out_a.float() - out_b.float()).abs().max()
+        ref = O.gva_decode_step(inp.V, inp.kr, inp.q_nope, inp.q_rope, inp.M, lens + i + 1, wl.scale, BASE, "bf16")
+        S.assert_close(S.host(out_b), ref, "bf16", f"fused step hpg={hpg} d_r={d_r} i={i}")
+    assert torch.equal(ca.v_cache, cb.v_cache)
+    assert torch.equal(ca.kr_cache, cb.kr_cache)
+
+
 def test_step_matches_oracle_mid():
     """Mid-workload shape (B=16, S=4096): prefill, then two fused steps, each
     against the oracle's step from pre-RoPE inputs."""
