@@ -79,9 +79,11 @@ gva_status check_shape(const gva_shape* s, bool gqa) {
 int resolve_split(const gva_shape* s) {
   if (s->split_tokens > 0) return s->split_tokens;
   // About one workgroup of (sequence, group, partition) per compute unit
-  // (256 of them; the decode kernel's register use allows one 512-thread
-  // workgroup per unit), each partition a whole number of 64-token tiles and
-  // at least one tile per wave of the eight-wave workgroup.
+  // (256 of them; the decode kernel's LDS use, about 92 KB per workgroup,
+  // allows one 512-thread workgroup per unit), so that all of them run in one
+  // round: a second round pays each workgroup's fixed prologue and split-K
+  // hand-off again. Each partition is a whole number of 64-token tiles, at
+  // least one per wave of the eight-wave workgroup.
   const int64_t base = (int64_t)s->B * s->G;
   const int64_t want_parts = (256 + base - 1) / base;
   const int64_t tiles = (s->max_seq_len + 63) / 64;
