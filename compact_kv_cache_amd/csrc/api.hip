@@ -85,8 +85,16 @@ int resolve_split(const gva_shape* s) {
   // hand-off again. Each partition is a whole number of 64-token tiles, at
   // least one per wave of the eight-wave workgroup.
   const int64_t base = (int64_t)s->B * s->G;
-  const int64_t want_parts = (256 + base - 1) / base;
+  int64_t want_parts = (256 + base - 1) / base;
   const int64_t tiles = (s->max_seq_len + 63) / 64;
+  // A batch that fills the units by itself (B*G >= 256) gets one partition
+  // per (sequence, group), and uneven lengths then leave the time to the
+  // longest sequences. When thirds of the longest stay long (>= 160 tiles),
+  // split into thirds instead: the dispatcher hands the extra pieces to the
+  // units that finish early. Measured on paged batches of 64 sequences:
+  // lengths uniform in [1024, 32768] 124 -> 116 us (decode), equal lengths
+  // of 32000 unchanged (186 us); shorter pieces cost more than they balance.
+  if (want_parts == 1 && tiles >= 3 * 160) want_parts = 3;
   int64_t tiles_per = (tiles + want_parts - 1) / want_parts;
   if (tiles_per < 8) tiles_per = 8;
   return (int)(tiles_per * 64);

@@ -83,19 +83,24 @@ def test_auto_split_is_multiple_of_64():
 
 
 @pytest.mark.parametrize("B,n", [(16, 4096), (16, 4196), (16, 2100), (32, 8192), (4, 131072),
-                                 (64, 32868), (1, 256), (3, 1100)])
+                                 (64, 32868), (64, 16960), (64, 30720), (1, 256), (3, 1100)])
 def test_auto_split_partitions(B, n):
     """Auto partitions: whole 64-token tiles, at least 8 per partition, and no
     more (sequence, group, partition) workgroups than the 256 compute units
-    when the sequences are long enough to need more than one partition."""
+    when the sequences are long enough to need more than one partition --
+    except a batch that fills the units by itself (B*G >= 256) with sequences
+    of at least 3 x 160 tiles, which is split into thirds of >= 160 tiles."""
     s = _shape(B=B, split_tokens=0, max_seq_len=n, capacity=max(n, 64))
     tiles_per = gva.gva_decode_split_tokens(s) // 64
     tiles = -(-n // 64)
     parts = -(-tiles // tiles_per)
     assert tiles_per >= 8
-    if parts > 1:
-        assert parts * B * 4 <= 256
     want = -(-256 // (B * 4))
+    if want == 1 and tiles >= 3 * 160:
+        want = 3
+        assert parts == 3 and tiles_per >= 160
+    elif parts > 1:
+        assert parts * B * 4 <= 256
     assert tiles_per == max(8, -(-tiles // want))
 
 
