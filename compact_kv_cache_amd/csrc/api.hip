@@ -76,6 +76,12 @@ gva_status check_shape(const gva_shape* s, bool gqa) {
   return GVA_OK;
 }
 
+// The automatic split of a batch that fills the units by itself (B*G >= 256)
+// when thirds of the longest sequence stay long (>= 160 tiles).
+bool thirds_split(const gva_shape* s) {
+  return s->split_tokens <= 0 && (int64_t)s->B * s->G >= 256 && (s->max_seq_len + 63) / 64 >= 3 * 160;
+}
+
 int resolve_split(const gva_shape* s) {
   if (s->split_tokens > 0) return s->split_tokens;
   // About one workgroup of (sequence, group, partition) per compute unit
@@ -94,7 +100,7 @@ int resolve_split(const gva_shape* s) {
   // units that finish early. Measured on paged batches of 64 sequences:
   // lengths uniform in [1024, 32768] 124 -> 116 us (decode), equal lengths
   // of 32000 unchanged (186 us); shorter pieces cost more than they balance.
-  if (want_parts == 1 && tiles >= 3 * 160) want_parts = 3;
+  if (thirds_split(s)) want_parts = 3;
   int64_t tiles_per = (tiles + want_parts - 1) / want_parts;
   if (tiles_per < 8) tiles_per = 8;
   return (int)(tiles_per * 64);

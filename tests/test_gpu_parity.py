@@ -236,6 +236,42 @@ def test_decode_full_size(name):
     S.assert_close(out, ref, wl.dtype, f"full {name}")
 
 
+def test_decode_auto_thirds_equals_plain_split():
+    """A batch that fills the compute units by itself (B*G = 256) with a few
+    sequences long enough for the automatic split into thirds (ties in length
+    included, one empty sequence): identical to the explicit split of the same
+    length, and within tolerance of the oracle."""
+    wl = W.Workload("ranked", 9, B=64, H=16, G=4, d_n=64, d_v=64, d_r=16, S=0, dtype="bf16")
+    rng = np.random.default_rng(61)
+    lens = rng.integers(1, 3000, size=wl.B)
+    lens[[5, 17, 40, 63]] = [30800, 31000, 30721, 30800]   # ties in length too
+    lens[3] = 0
+    inp = W.make_gva_inputs(wl, lens=lens, seed=62)
+    kr_rot, q_rot = W.draw_post_rope(wl, inp.lens, seed=62)
+    cap = int(lens.max())
+    v, k, table, nblk = S.paged_cache_from_host(wl, inp.V, kr_rot, np.maximum(lens, 1), 63)
+    seq = torch.tensor(lens.astype(np.int32), device="cuda")
+    qn, qr, Md = (S.dev(x, "bf16") for x in (inp.q_nope, q_rot, inp.M))
+
+    def shape(split):
+        return gva.make_shape(wl.B, wl.H, wl.G, 64, 64, wl.d_r, max_seq_len=cap, block_size=64, num_blocks=nblk,
+                              max_blocks_per_seq=table.shape[1], split_tokens=split, dtype="bf16")
+    s_auto = shape(0)
+    auto = gva.gva_decode_split_tokens(s_auto)
+    assert 3 * auto >= cap > 2 * auto, "the automatic split cuts the longest sequences into thirds"
+    s_plain = shape(auto)
+    outs = []
+    for label, sh in (("auto", s_auto), ("explicit", s_plain)):
+        print(f"[case] decode thirds {label} split={auto}", flush=True)
+        out = torch.full((wl.B, wl.H, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+        gva.gva_decode(sh, qn, qr, Md, v, k, seq, table, wl.scale, out, S.workspace(sh))
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1])
+    ref = O.gva_decode(inp.V, kr_rot, inp.q_nope, q_rot, inp.M, lens, wl.scale)
+    S.assert_close(S.host(outs[0]), ref, "bf16", "auto thirds")
+
+
 def test_decode_mid_bf16_end_to_end_steps():
     """Mid workload through the whole path: prefill 4096 tokens with
     gva_append, then three steps of {append one token, rotate the query,
