@@ -80,7 +80,11 @@ typedef enum gva_dtype {
  *   num_blocks       paged: blocks in the pool
  *   max_blocks_per_seq  paged: row stride of block_table
  *   split_tokens     split-K partition length in tokens for decode
- *                    (0 = automatic; otherwise a positive multiple of 64)
+ *                    (0 = automatic; otherwise a positive multiple of 64).
+ *                    Automatic: partitions of whole 64-token tiles, at least
+ *                    512 tokens, sized so that the B*G*partitions workgroups
+ *                    fill the 256 compute units in one round; when B*G >= 256
+ *                    and the longest sequence has >= 480 tiles, thirds of it.
  *   dtype            storage dtype of q, M, caches and out
  *
  * Cache layouts (call dtype):
