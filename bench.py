@@ -293,6 +293,11 @@ def main():
 
     traffic = recorded_traffic(wl.name)
 
+    # partition length(s) of the lengths the recorded steps ran at (the
+    # automatic choice depends on the number of 64-token tiles)
+    splits = sorted({gva.gva_decode_split_tokens(shape_at(0, int(round(b / (wl.B * bpt)))))
+                     for b in step_bytes})
+    split_used = splits[0] if len(splits) == 1 else splits
     result = {
         "metric": METRIC,
         "value": round(1e3 / ms_per_step, 2),
@@ -310,7 +315,7 @@ def main():
                                f"G={wl.G} d_n={wl.d_n} d_v={wl.d_v} d_r={wl.d_r} {wl.dtype}, "
                                f"contiguous cache, {R} cold replicas",
                    "B": wl.B, "S": wl.S, "H": wl.H, "G": wl.G, "d_v": wl.d_v, "d_r": wl.d_r,
-                   "replicas": R, "split_tokens": gva.gva_decode_split_tokens(shape_at(0, wl.S)),
+                   "replicas": R, "split_tokens": split_used,
                    "graph": use_graph, "step": "gva_decode_step (one launch)"},
         "cache_read_GBps": round(mean_step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "step_kernel_us": round(ms_step * 1e3, 3),
