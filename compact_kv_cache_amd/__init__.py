@@ -44,11 +44,17 @@ def make_shape(B: int, H: int, G: int, d_n: int, d_v: int, d_r: int, *, capacity
                     max_blocks_per_seq, split_tokens, _DTYPES[dtype])
 
 
-def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype], what: str):
+def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype], what: str, numel: int = 0):
+    """Device pointer of `t` after checking it: a contiguous device tensor of
+    `dtype` holding at least `numel` elements (the extent the C call will
+    touch for the given shape; a shorter tensor would be read or written out
+    of bounds by the kernels)."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{what} must be a torch.Tensor")
+    if t.numel() < numel:
+        raise ValueError(f"{what} holds {t.numel()} elements; the shape needs at least {numel}")
     if t.device.type != "cuda":
         raise ValueError(f"{what} must be a device tensor (got {t.device})")
     if not t.is_contiguous():
@@ -56,6 +62,24 @@ def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype], what: str):
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{what} has dtype {t.dtype}, expected {dtype}")
     return t.data_ptr()
+
+
+def _n_cache(shape: GvaShape, width: int) -> int:
+    """Elements of a value-like cache ([.., G, .., width]) for `shape`."""
+    if shape.block_size:
+        return shape.num_blocks * shape.G * 64 * width
+    return shape.B * shape.G * shape.capacity * width
+
+
+def _n_kr(shape: GvaShape) -> int:
+    """Elements of the positional-key cache for `shape`."""
+    if shape.block_size:
+        return shape.num_blocks * 64 * shape.d_r
+    return shape.B * shape.capacity * shape.d_r
+
+
+def _n_table(shape: GvaShape) -> int:
+    return shape.B * shape.max_blocks_per_seq if shape.block_size else 0
 
 
 def _stream(stream) -> Optional[int]:
@@ -72,19 +96,23 @@ def _check(status: int, fn: str):
 def gva_append(shape: GvaShape, v_new, kr_new, n_new: int, seq_lens, v_cache, kr_cache,
                block_table=None, rope_base: float = 10000.0, stream=None) -> None:
     dt = _TORCH.get(shape.dtype)
-    _check(lib.gva_append(shape, _ptr(v_new, dt, "v_new"), _ptr(kr_new, dt, "kr_new"), int(n_new),
-                          _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(v_cache, dt, "v_cache"),
-                          _ptr(kr_cache, dt, "kr_cache"),
-                          _ptr(block_table, torch.int32, "block_table"), float(rope_base),
+    B, G, nn = shape.B, shape.G, max(int(n_new), 0)
+    _check(lib.gva_append(shape, _ptr(v_new, dt, "v_new", B * G * nn * shape.d_v),
+                          _ptr(kr_new, dt, "kr_new", B * nn * shape.d_r), int(n_new),
+                          _ptr(seq_lens, torch.int32, "seq_lens", B),
+                          _ptr(v_cache, dt, "v_cache", _n_cache(shape, shape.d_v)),
+                          _ptr(kr_cache, dt, "kr_cache", _n_kr(shape)),
+                          _ptr(block_table, torch.int32, "block_table", _n_table(shape)), float(rope_base),
                           _stream(stream)), "gva_append")
 
 
 def gva_rope_query(shape: GvaShape, q_rope_in, q_rope_out, seq_lens, rope_base: float = 10000.0,
                    stream=None) -> None:
     dt = _TORCH.get(shape.dtype)
-    _check(lib.gva_rope_query(shape, _ptr(q_rope_in, dt, "q_rope_in"),
-                              _ptr(q_rope_out, dt, "q_rope_out"),
-                              _ptr(seq_lens, torch.int32, "seq_lens"), float(rope_base),
+    nr = shape.B * shape.H * shape.d_r
+    _check(lib.gva_rope_query(shape, _ptr(q_rope_in, dt, "q_rope_in", nr),
+                              _ptr(q_rope_out, dt, "q_rope_out", nr),
+                              _ptr(seq_lens, torch.int32, "seq_lens", shape.B), float(rope_base),
                               _stream(stream)), "gva_rope_query")
 
 
@@ -92,11 +120,15 @@ def gva_decode(shape: GvaShape, q_nope, q_rope, M, v_cache, kr_cache, seq_lens, 
                scale: float, out, workspace=None, stream=None) -> None:
     dt = _TORCH.get(shape.dtype)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.gva_decode(shape, _ptr(q_nope, dt, "q_nope"), _ptr(q_rope, dt, "q_rope"),
-                          _ptr(M, dt, "M"), _ptr(v_cache, dt, "v_cache"),
-                          _ptr(kr_cache, dt, "kr_cache"), _ptr(seq_lens, torch.int32, "seq_lens"),
-                          _ptr(block_table, torch.int32, "block_table"), float(scale),
-                          _ptr(out, dt, "out"), _ptr(workspace, None, "workspace"), ws_bytes,
+    B, H = shape.B, shape.H
+    _check(lib.gva_decode(shape, _ptr(q_nope, dt, "q_nope", B * H * shape.d_n),
+                          _ptr(q_rope, dt, "q_rope", B * H * shape.d_r),
+                          _ptr(M, dt, "M", H * shape.d_v * shape.d_n),
+                          _ptr(v_cache, dt, "v_cache", _n_cache(shape, shape.d_v)),
+                          _ptr(kr_cache, dt, "kr_cache", _n_kr(shape)),
+                          _ptr(seq_lens, torch.int32, "seq_lens", B),
+                          _ptr(block_table, torch.int32, "block_table", _n_table(shape)), float(scale),
+                          _ptr(out, dt, "out", B * H * shape.d_v), _ptr(workspace, None, "workspace"), ws_bytes,
                           _stream(stream)), "gva_decode")
 
 
@@ -104,13 +136,17 @@ def gva_decode_step(shape: GvaShape, v_new, kr_new, q_nope, q_rope, M, v_cache, 
                     block_table, scale: float, rope_base: float, out, workspace, stream=None) -> None:
     dt = _TORCH.get(shape.dtype)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.gva_decode_step(shape, _ptr(v_new, dt, "v_new"), _ptr(kr_new, dt, "kr_new"),
-                               _ptr(q_nope, dt, "q_nope"), _ptr(q_rope, dt, "q_rope"),
-                               _ptr(M, dt, "M"), _ptr(v_cache, dt, "v_cache"),
-                               _ptr(kr_cache, dt, "kr_cache"),
-                               _ptr(seq_lens, torch.int32, "seq_lens"),
-                               _ptr(block_table, torch.int32, "block_table"), float(scale),
-                               float(rope_base), _ptr(out, dt, "out"),
+    B, H, G = shape.B, shape.H, shape.G
+    _check(lib.gva_decode_step(shape, _ptr(v_new, dt, "v_new", B * G * shape.d_v),
+                               _ptr(kr_new, dt, "kr_new", B * shape.d_r),
+                               _ptr(q_nope, dt, "q_nope", B * H * shape.d_n),
+                               _ptr(q_rope, dt, "q_rope", B * H * shape.d_r),
+                               _ptr(M, dt, "M", H * shape.d_v * shape.d_n),
+                               _ptr(v_cache, dt, "v_cache", _n_cache(shape, shape.d_v)),
+                               _ptr(kr_cache, dt, "kr_cache", _n_kr(shape)),
+                               _ptr(seq_lens, torch.int32, "seq_lens", B),
+                               _ptr(block_table, torch.int32, "block_table", _n_table(shape)), float(scale),
+                               float(rope_base), _ptr(out, dt, "out", B * H * shape.d_v),
                                _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream)),
            "gva_decode_step")
 
@@ -118,9 +154,10 @@ def gva_decode_step(shape: GvaShape, v_new, kr_new, q_nope, q_rope, M, v_cache, 
 def gva_rope_query_multi(shape: GvaShape, n_q: int, q_rope_in, q_rope_out, seq_lens,
                          rope_base: float = 10000.0, stream=None) -> None:
     dt = _TORCH.get(shape.dtype)
-    _check(lib.gva_rope_query_multi(shape, int(n_q), _ptr(q_rope_in, dt, "q_rope_in"),
-                                    _ptr(q_rope_out, dt, "q_rope_out"),
-                                    _ptr(seq_lens, torch.int32, "seq_lens"), float(rope_base),
+    nr = shape.B * max(int(n_q), 0) * shape.H * shape.d_r
+    _check(lib.gva_rope_query_multi(shape, int(n_q), _ptr(q_rope_in, dt, "q_rope_in", nr),
+                                    _ptr(q_rope_out, dt, "q_rope_out", nr),
+                                    _ptr(seq_lens, torch.int32, "seq_lens", shape.B), float(rope_base),
                                     _stream(stream)), "gva_rope_query_multi")
 
 
@@ -128,11 +165,15 @@ def gva_decode_multi(shape: GvaShape, n_q: int, q_nope, q_rope, M, v_cache, kr_c
                      block_table, scale: float, out, workspace=None, stream=None) -> None:
     dt = _TORCH.get(shape.dtype)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.gva_decode_multi(shape, int(n_q), _ptr(q_nope, dt, "q_nope"), _ptr(q_rope, dt, "q_rope"),
-                                _ptr(M, dt, "M"), _ptr(v_cache, dt, "v_cache"),
-                                _ptr(kr_cache, dt, "kr_cache"), _ptr(seq_lens, torch.int32, "seq_lens"),
-                                _ptr(block_table, torch.int32, "block_table"), float(scale),
-                                _ptr(out, dt, "out"), _ptr(workspace, None, "workspace"), ws_bytes,
+    BQH = shape.B * max(int(n_q), 0) * shape.H
+    _check(lib.gva_decode_multi(shape, int(n_q), _ptr(q_nope, dt, "q_nope", BQH * shape.d_n),
+                                _ptr(q_rope, dt, "q_rope", BQH * shape.d_r),
+                                _ptr(M, dt, "M", shape.H * shape.d_v * shape.d_n),
+                                _ptr(v_cache, dt, "v_cache", _n_cache(shape, shape.d_v)),
+                                _ptr(kr_cache, dt, "kr_cache", _n_kr(shape)),
+                                _ptr(seq_lens, torch.int32, "seq_lens", shape.B),
+                                _ptr(block_table, torch.int32, "block_table", _n_table(shape)), float(scale),
+                                _ptr(out, dt, "out", BQH * shape.d_v), _ptr(workspace, None, "workspace"), ws_bytes,
                                 _stream(stream)), "gva_decode_multi")
 
 
@@ -146,10 +187,15 @@ def gva_prefill(shape: GvaShape, n_q: int, q_nope, q_rope, M, v_cache, kr_cache,
     bf16): q_nope [B, n_q, H, d_n], q_rope [B, n_q, H, d_r] rotated, out
     [B, n_q, H, d_v]."""
     dt = _TORCH.get(shape.dtype)
-    _check(lib.gva_prefill(shape, int(n_q), _ptr(q_nope, dt, "q_nope"), _ptr(q_rope, dt, "q_rope"),
-                           _ptr(M, dt, "M"), _ptr(v_cache, dt, "v_cache"), _ptr(kr_cache, dt, "kr_cache"),
-                           _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(block_table, torch.int32, "block_table"),
-                           float(scale), _ptr(out, dt, "out"), _stream(stream)), "gva_prefill")
+    BQH = shape.B * max(int(n_q), 0) * shape.H
+    _check(lib.gva_prefill(shape, int(n_q), _ptr(q_nope, dt, "q_nope", BQH * shape.d_n),
+                           _ptr(q_rope, dt, "q_rope", BQH * shape.d_r),
+                           _ptr(M, dt, "M", shape.H * shape.d_v * shape.d_n),
+                           _ptr(v_cache, dt, "v_cache", _n_cache(shape, shape.d_v)),
+                           _ptr(kr_cache, dt, "kr_cache", _n_kr(shape)),
+                           _ptr(seq_lens, torch.int32, "seq_lens", shape.B),
+                           _ptr(block_table, torch.int32, "block_table", _n_table(shape)),
+                           float(scale), _ptr(out, dt, "out", BQH * shape.d_v), _stream(stream)), "gva_prefill")
 
 
 def gva_copy_blocks(shape: GvaShape, src_blocks, dst_blocks, v_cache, kr_cache, block_table=None,
@@ -163,8 +209,10 @@ def gva_copy_blocks(shape: GvaShape, src_blocks, dst_blocks, v_cache, kr_cache, 
     _check(lib.gva_copy_blocks(shape, _ptr(src_blocks, torch.int32, "src_blocks"),
                                _ptr(dst_blocks, torch.int32, "dst_blocks"), n,
                                _ptr(remap_seqs, torch.int32, "remap_seqs"),
-                               _ptr(remap_slots, torch.int32, "remap_slots"), _ptr(v_cache, dt, "v_cache"),
-                               _ptr(kr_cache, dt, "kr_cache"), _ptr(block_table, torch.int32, "block_table"),
+                               _ptr(remap_slots, torch.int32, "remap_slots", n if remap_seqs is not None else 0),
+                               _ptr(v_cache, dt, "v_cache", _n_cache(shape, shape.d_v)),
+                               _ptr(kr_cache, dt, "kr_cache", _n_kr(shape)),
+                               _ptr(block_table, torch.int32, "block_table", _n_table(shape)),
                                _stream(stream)), "gva_copy_blocks")
 
 
@@ -173,12 +221,13 @@ def gva_fork(shape: GvaShape, src_seqs, dst_seqs, seq_lens, block_table, stream=
     if int(dst_seqs.numel()) != n:
         raise ValueError("src_seqs and dst_seqs must have the same length")
     _check(lib.gva_fork(shape, _ptr(src_seqs, torch.int32, "src_seqs"), _ptr(dst_seqs, torch.int32, "dst_seqs"),
-                        n, _ptr(seq_lens, torch.int32, "seq_lens"),
-                        _ptr(block_table, torch.int32, "block_table"), _stream(stream)), "gva_fork")
+                        n, _ptr(seq_lens, torch.int32, "seq_lens", shape.B),
+                        _ptr(block_table, torch.int32, "block_table", _n_table(shape)), _stream(stream)), "gva_fork")
 
 
 def gva_rollback(shape: GvaShape, seq_lens, n_drop, stream=None) -> None:
-    _check(lib.gva_rollback(shape, _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(n_drop, torch.int32, "n_drop"),
+    _check(lib.gva_rollback(shape, _ptr(seq_lens, torch.int32, "seq_lens", shape.B),
+                            _ptr(n_drop, torch.int32, "n_drop", shape.B),
                             _stream(stream)), "gva_rollback")
 
 
@@ -206,9 +255,12 @@ def gva_query_projection(shape: GvaShape, x, w_fold, w_rope, q_abs, q_rope, stre
     x [B, d_model], w_fold [H, d_v, d_model], w_rope [H, d_r, d_model]."""
     dt = _TORCH.get(shape.dtype)
     d_model = x.shape[-1]
-    _check(lib.gva_query_projection(shape, int(d_model), _ptr(x, dt, "x"), _ptr(w_fold, dt, "w_fold"),
-                                    _ptr(w_rope, dt, "w_rope"), _ptr(q_abs, dt, "q_abs"),
-                                    _ptr(q_rope, dt, "q_rope"), _stream(stream)),
+    B, H = shape.B, shape.H
+    _check(lib.gva_query_projection(shape, int(d_model), _ptr(x, dt, "x", B * d_model),
+                                    _ptr(w_fold, dt, "w_fold", H * shape.d_v * d_model),
+                                    _ptr(w_rope, dt, "w_rope", H * shape.d_r * d_model),
+                                    _ptr(q_abs, dt, "q_abs", B * H * shape.d_v),
+                                    _ptr(q_rope, dt, "q_rope", B * H * shape.d_r), _stream(stream)),
            "gva_query_projection")
 
 
@@ -216,11 +268,13 @@ def gva_gqa_ref_decode(shape: GvaShape, q, k_cache, v_cache, seq_lens, block_tab
                        out, workspace=None, stream=None) -> None:
     dt = _TORCH.get(shape.dtype)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.gva_gqa_ref_decode(shape, _ptr(q, dt, "q"), _ptr(k_cache, dt, "k_cache"),
-                                  _ptr(v_cache, dt, "v_cache"),
-                                  _ptr(seq_lens, torch.int32, "seq_lens"),
-                                  _ptr(block_table, torch.int32, "block_table"), float(scale),
-                                  _ptr(out, dt, "out"), _ptr(workspace, None, "workspace"),
+    B, H = shape.B, shape.H
+    _check(lib.gva_gqa_ref_decode(shape, _ptr(q, dt, "q", B * H * shape.d_n),
+                                  _ptr(k_cache, dt, "k_cache", _n_cache(shape, shape.d_n)),
+                                  _ptr(v_cache, dt, "v_cache", _n_cache(shape, shape.d_v)),
+                                  _ptr(seq_lens, torch.int32, "seq_lens", B),
+                                  _ptr(block_table, torch.int32, "block_table", _n_table(shape)), float(scale),
+                                  _ptr(out, dt, "out", B * H * shape.d_v), _ptr(workspace, None, "workspace"),
                                   ws_bytes, _stream(stream)), "gva_gqa_ref_decode")
 
 

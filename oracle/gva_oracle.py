@@ -362,9 +362,3 @@ def gqa_decode(q, K, V, seq_lens, scale: float) -> np.ndarray:
             s = float(scale) * (Kg @ np.asarray(q[b, h], dtype=np.float64))
             out[b, h] = _softmax(s) @ Vg
     return out
-
-
-def decode_flops_materialized(B: int, H: int, n_mean: float, d_v: int, d_n: int, d_r: int) -> float:
-    """Work of this oracle per decode: key materialization plus scores and
-    value sum (used to size the CPU-baseline sample)."""
-    return 2.0 * B * H * n_mean * (d_v * d_n + (d_n + d_r) + d_v)

@@ -178,3 +178,56 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(16, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         gva.gva_decode(s, x, x, x, x, x, torch.zeros(1, dtype=torch.int32), None, 0.1, x)
+
+
+def _short_size_error(fn, *args):
+    """The wrapper must refuse before the C call: a size error, not the
+    device check that a host tensor of the right size would reach."""
+    with pytest.raises(ValueError, match="elements"):
+        fn(*args)
+
+
+def test_binding_rejects_short_tensors():
+    import torch
+    bf = torch.bfloat16
+    B, H, G, cap = 2, 16, 4, 128
+    s = _shape(B=B, split_tokens=0, max_seq_len=cap, capacity=cap)
+    z = lambda *shape, dt=bf: torch.zeros(*shape, dtype=dt)  # noqa: E731
+    q, qr, M = z(B, H, 64), z(B, H, 16), z(H, 64, 64)
+    vc, kc = z(B, G, cap, 64), z(B, cap, 16)
+    lens, out = z(B, dt=torch.int32), z(B, H, 64)
+    # every tensor of the decode one element short (the tensors before it are
+    # passed as None, so that the short one is the first the binding checks)
+    tensor_slots = [0, 1, 2, 3, 4, 5, 8]
+    for slot in tensor_slots:
+        args = [q, qr, M, vc, kc, lens, None, 0.1, out]
+        for j in tensor_slots:
+            if j < slot:
+                args[j] = None
+        args[slot] = args[slot].reshape(-1)[:-1].clone()
+        _short_size_error(gva.gva_decode, s, *args)
+    # the fused step's new-token tensors and the append's
+    _short_size_error(gva.gva_decode_step, s, z(B, G, 63), z(B, 16), q, qr, M, vc, kc, lens, None,
+                      0.1, 10000.0, out, None)
+    _short_size_error(gva.gva_decode_step, s, None, z(B * 16 - 1), q, qr, M, vc, kc, lens,
+                      None, 0.1, 10000.0, out, None)
+    _short_size_error(gva.gva_append, s, z(B, G, 3, 64), z(B, 4, 16), 4, lens, vc, kc)
+    # a paged cache: the table and the pool size come from the shape
+    sp = gva.make_shape(B, H, G, 64, 64, 16, max_seq_len=128, block_size=64, num_blocks=8,
+                        max_blocks_per_seq=2)
+    _short_size_error(gva.gva_decode, sp, None, None, None, None, None, None,
+                      z(3, dt=torch.int32), 0.1, out)
+    _short_size_error(gva.gva_decode, sp, None, None, None, z(7, G, 64, 64), z(8, 64, 16), lens,
+                      z(4, dt=torch.int32), 0.1, out)
+    _short_size_error(gva.gva_rollback, sp, None, z(B - 1, dt=torch.int32))
+    _short_size_error(gva.gva_rope_query, s, None, z(B * H * 16 - 1), lens)
+
+
+def test_binding_right_sizes_reach_the_device_check():
+    import torch
+    B, cap = 2, 128
+    s = _shape(B=B, split_tokens=0, max_seq_len=cap, capacity=cap)
+    z = lambda *shape, dt=torch.bfloat16: torch.zeros(*shape, dtype=dt)  # noqa: E731
+    with pytest.raises(ValueError, match="device tensor"):
+        gva.gva_decode(s, z(B, 16, 64), z(B, 16, 16), z(16, 64, 64), z(B, 4, cap, 64), z(B, cap, 16),
+                       z(B, dt=torch.int32), None, 0.1, z(B, 16, 64))
