@@ -9,7 +9,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libgva.so")
+# GVA_LIBRARY names another build of the same library (for instance the
+# host-sanitized one that the CPU test suite builds); default: the in-tree one.
+LIB_PATH = os.environ.get("GVA_LIBRARY") or os.path.join(_PKG, "libgva.so")
 
 GVA_OK = 0
 GVA_ERR_INVALID_ARGUMENT = 1
