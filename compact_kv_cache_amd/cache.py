@@ -106,3 +106,32 @@ class GvaCache:
             workspace = self.step_workspace(max_seq_len, split_tokens)
         gva_decode_step(shape, v_new, kr_new, q_nope, q_rope, M, self.v_cache, self.kr_cache,
                         self.seq_lens, self.block_table, scale, rope_base, out, workspace, stream)
+
+    def snapshot(self) -> dict:
+        """Host copy of the cache state (checkpoint): both caches, the lengths
+        and, for a paged cache, the block table. Synchronous device-to-host
+        copies; the state of the device tensors is unchanged."""
+        state = {"v_cache": self.v_cache.cpu(), "seq_lens": self.seq_lens.cpu()}
+        if self.kr_cache is not None:
+            state["kr_cache"] = self.kr_cache.cpu()
+        if self.block_table is not None:
+            state["block_table"] = self.block_table.cpu()
+        return state
+
+    def restore(self, state: dict) -> None:
+        """Put a snapshot() back into this cache's device tensors (resume). The
+        snapshot must come from a cache of the same sizes and layout."""
+        pairs = [("v_cache", self.v_cache), ("seq_lens", self.seq_lens),
+                 ("kr_cache", self.kr_cache), ("block_table", self.block_table)]
+        for name, dst in pairs:
+            if (dst is None) != (name not in state):
+                raise ValueError(f"snapshot and cache disagree on {name}")
+            if dst is None:
+                continue
+            src = state[name]
+            if tuple(src.shape) != tuple(dst.shape) or src.dtype != dst.dtype:
+                raise ValueError(f"{name}: snapshot {tuple(src.shape)} {src.dtype} does not fit "
+                                 f"{tuple(dst.shape)} {dst.dtype}")
+        for name, dst in pairs:
+            if dst is not None:
+                dst.copy_(state[name])

@@ -119,7 +119,7 @@ void set_workspace(gva::DecodeLaunch& a, void* workspace) {
   if (!workspace) return;
   char* base = static_cast<char*>(workspace);
   a.counters = reinterpret_cast<int32_t*>(base);
-  a.counters_seq = a.counters + (size_t)a.B * a.G;
+  a.counters_seq = a.counters + (size_t)a.B * a.G * gva::kCounterStride;
   a.ws_o = reinterpret_cast<float*>(base + gva::ws_counter_bytes(a.B, a.G));
   a.ws_ml = a.ws_o + (size_t)a.B * a.nq * a.H * a.n_split * 64;
 }

@@ -300,10 +300,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
   auto arrive_seq = [&]() {  // thread kSeqThread
     if constexpr (STEP) {
       const int ticket =
-          __hip_atomic_fetch_add(a.counters_seq + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(a.counters_seq + (int64_t)b * kCounterStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (ticket == seq_arrivals - 1) {
         a.seq_lens_rw[b] = n_full;
-        __hip_atomic_store(a.counters_seq + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.counters_seq + (int64_t)b * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   };
@@ -640,7 +640,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
       }
     }
   }
-  int32_t* counter = a.counters + (int64_t)b * G + g;
+  int32_t* counter = a.counters + ((int64_t)b * G + g) * kCounterStride;
   if (arrive_last(counter, n_parts)) {
     if (tid == kSeqThread) arrive_seq();
 #pragma unroll

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeLaunch a) {
       st_dev(a.ws_ml + 2 * (slot0 + split) + 1, l);
     }
   }
-  int32_t* counter = a.counters + (int64_t)b * a.G + g;
+  int32_t* counter = a.counters + ((int64_t)b * a.G + g) * kCounterStride;
   if (!arrive_last(counter, n_parts)) return;
   if (w < HPG)
     out[((int64_t)b * H + h) * kD + lane] =

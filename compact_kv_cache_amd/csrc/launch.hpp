@@ -93,19 +93,23 @@ struct DecodeLaunch {
 };
 
 // Workspace layout (bytes): counters, partials, rotated-query scratch.
+// Arrival counters sit 128 bytes apart: device-scope atomics on one cache
+// line are serialized (about 11 ns each), so counters of different groups
+// sharing a line would queue each other's arrivals.
+constexpr int kCounterStride = 32;  // int32 slots per counter
 inline size_t ws_counter_bytes(int B, int G) {
-  return (((size_t)B * G + B) * 4 + 255) / 256 * 256;
+  return (((size_t)B * G + B) * kCounterStride * 4 + 255) / 256 * 256;
 }
-inline size_t ws_partial_bytes(int B, int H, int n_split) {
-  return n_split <= 1 ? 0 : (size_t)B * H * n_split * (64 + 2) * sizeof(float);
+inline size_t ws_partial_bytes(int B, int H, int n_split, int nq) {
+  return n_split <= 1 ? 0 : (size_t)B * nq * H * n_split * (64 + 2) * sizeof(float);
 }
 inline size_t ws_qrot_bytes(int B, int H) { return (((size_t)B * H * 32 * 4) + 255) / 256 * 256; }
 inline size_t ws_total_bytes(int B, int H, int G, int n_split, int nq = 1) {
   if (n_split <= 1) return 0;
-  return ws_counter_bytes(B, G) + ws_partial_bytes(B * nq, H, n_split);
+  return ws_counter_bytes(B, G) + ws_partial_bytes(B, H, n_split, nq);
 }
 inline size_t ws_step_bytes(int B, int H, int G, int n_split) {
-  return ws_counter_bytes(B, G) + ws_partial_bytes(B, H, n_split) + ws_qrot_bytes(B, H);
+  return ws_counter_bytes(B, G) + ws_partial_bytes(B, H, n_split, 1) + ws_qrot_bytes(B, H);
 }
 
 // Offline fold of the reconstruction maps into the query projection:

@@ -69,9 +69,9 @@ def _shape(**kw):
 def test_workspace_size_long_split():
     s = _shape()
     assert gva.gva_decode_split_tokens(s) == 4096
-    # 256 bytes of arrival counters (B * G int32, padded), then
+    # arrival counters (B * G + B of them, one per 128-byte line), then
     # B * H * 32 partitions * (64 + 2) floats of partials
-    assert gva.gva_decode_workspace_bytes(s) == 256 + 4 * 16 * 32 * 66 * 4 == 256 + 540672
+    assert gva.gva_decode_workspace_bytes(s) == (16 + 4) * 128 + 4 * 16 * 32 * 66 * 4 == 2560 + 540672
     assert gva.gva_decode_workspace_bytes(_shape(max_seq_len=4096)) == 0
 
 

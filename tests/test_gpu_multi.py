@@ -158,12 +158,16 @@ def test_multi_mid_size_sampled():
 
 def test_multi_validation():
     shape = gva.make_shape(2, 16, 4, 64, 64, 16, capacity=64, max_seq_len=64, dtype="bf16")
+    # tensors of the sizes the shape needs, so that the library's own check
+    # (not the binding's size check) refuses the call
     t = torch.zeros(2, 4, 16, 64, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros(2, 4, 64, 64, dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros(2, 64, 16, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(gva.GvaError, match="n_q = 3"):
-        gva.gva_decode_multi(shape, 3, t, t, None, t, t, torch.zeros(2, dtype=torch.int32, device="cuda"),
+        gva.gva_decode_multi(shape, 3, t, t, None, vc, kc, torch.zeros(2, dtype=torch.int32, device="cuda"),
                              None, 0.1, t)
     shape32 = gva.make_shape(2, 16, 4, 64, 64, 16, capacity=64, max_seq_len=64, dtype="f32")
     t32 = torch.zeros(2, 4, 16, 64, dtype=torch.float32, device="cuda")
     with pytest.raises(gva.GvaError, match="bf16"):
-        gva.gva_decode_multi(shape32, 2, t32, t32, None, t32, t32,
+        gva.gva_decode_multi(shape32, 2, t32, t32, None, vc.float(), kc.float(),
                              torch.zeros(2, dtype=torch.int32, device="cuda"), None, 0.1, t32)
