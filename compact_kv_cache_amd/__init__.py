@@ -16,7 +16,8 @@ from ._lib import GVA_BF16, GVA_F32, GvaShape
 
 __all__ = [
     "GvaShape", "GVA_F32", "GVA_BF16", "GvaError", "make_shape", "lib",
-    "gva_append", "gva_rope_query", "gva_decode", "gva_decode_step", "gva_gqa_ref_decode",
+    "gva_append", "gva_rope_query", "gva_decode", "gva_decode_step", "gva_decode_step_noalloc",
+    "gva_gqa_ref_decode",
     "gva_fold_query_projection", "gva_query_projection", "gva_rope_query_multi", "gva_decode_multi",
     "gva_decode_multi_workspace_bytes", "gva_prefill", "gva_copy_blocks", "gva_fork", "gva_rollback",
     "gva_decode_workspace_bytes", "gva_decode_step_workspace_bytes", "gva_decode_split_tokens", "gva_cache_bytes_per_token",
@@ -149,6 +150,26 @@ def gva_decode_step(shape: GvaShape, v_new, kr_new, q_nope, q_rope, M, v_cache, 
                                float(rope_base), _ptr(out, dt, "out", B * H * shape.d_v),
                                _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream)),
            "gva_decode_step")
+
+
+def gva_decode_step_noalloc(shape: GvaShape, v_new, kr_new, q_nope, q_rope, M, v_cache, kr_cache, seq_lens,
+                            block_table, scale: float, rope_base: float, out, stream=None) -> None:
+    """gva_decode_step without a workspace: the library's fixed per-device
+    scratch (4 MiB) serves the split-K partials. Calls that overlap in time on
+    one device race."""
+    dt = _TORCH.get(shape.dtype)
+    B, H, G = shape.B, shape.H, shape.G
+    _check(lib.gva_decode_step_noalloc(shape, _ptr(v_new, dt, "v_new", B * G * shape.d_v),
+                                       _ptr(kr_new, dt, "kr_new", B * shape.d_r),
+                                       _ptr(q_nope, dt, "q_nope", B * H * shape.d_n),
+                                       _ptr(q_rope, dt, "q_rope", B * H * shape.d_r),
+                                       _ptr(M, dt, "M", H * shape.d_v * shape.d_n),
+                                       _ptr(v_cache, dt, "v_cache", _n_cache(shape, shape.d_v)),
+                                       _ptr(kr_cache, dt, "kr_cache", _n_kr(shape)),
+                                       _ptr(seq_lens, torch.int32, "seq_lens", B),
+                                       _ptr(block_table, torch.int32, "block_table", _n_table(shape)),
+                                       float(scale), float(rope_base), _ptr(out, dt, "out", B * H * shape.d_v),
+                                       _stream(stream)), "gva_decode_step_noalloc")
 
 
 def gva_rope_query_multi(shape: GvaShape, n_q: int, q_rope_in, q_rope_out, seq_lens,

@@ -47,6 +47,8 @@ SIGNATURES = {
     "gva_decode_step": (ctypes.c_int, [_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        ctypes.c_float, ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]),
     "gva_decode_step_workspace_bytes": (ctypes.c_size_t, [_shp]),
+    "gva_decode_step_noalloc": (ctypes.c_int, [_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                               ctypes.c_float, ctypes.c_float, _vp, _vp]),
     "gva_rope_query_multi": (ctypes.c_int, [_shp, _i32, _vp, _vp, _vp, ctypes.c_float, _vp]),
     "gva_decode_multi": (ctypes.c_int, [_shp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                         _vp, ctypes.c_size_t, _vp]),

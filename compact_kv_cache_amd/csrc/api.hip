@@ -159,6 +159,16 @@ gva::DecodeLaunch make_decode(const gva_shape* s) {
 
 }  // namespace
 
+namespace gva {
+gva_status refuse_scratch(size_t need, size_t have) {
+  return fail(GVA_ERR_WORKSPACE,
+              "the shape needs %zu bytes of split-K scratch; the allocation-free entry point holds %zu "
+              "(and up to 512 arrival counters, B*G + B)",
+              need, have);
+}
+gva_status hip_failure(hipError_t e, const char* what) { return hip_status(e, what); }
+}  // namespace gva
+
 extern "C" {
 
 gva_status gva_append(const gva_shape* shape, const void* v_new, const void* kr_new, int32_t n_new,

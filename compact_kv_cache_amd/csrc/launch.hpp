@@ -7,6 +7,8 @@
 
 #include <cmath>
 
+#include "../../include/gva.h"
+
 namespace gva {
 
 // RoPE frequencies theta_i = base^(-2i/d_r) for the d_r/2 channel pairs,
@@ -153,6 +155,10 @@ struct ForkLaunch {
   int32_t* seq_lens;
   int32_t* block_table;
 };
+
+// Status reporting of the C ABI layer (sets the thread's gva_last_error text).
+gva_status refuse_scratch(size_t need, size_t have);
+gva_status hip_failure(hipError_t e, const char* what);
 
 hipError_t launch_copy_blocks(const CopyBlocksLaunch& a, hipStream_t s);
 hipError_t launch_fork(const ForkLaunch& a, hipStream_t s);

@@ -276,6 +276,27 @@ gva_status gva_decode_step(const gva_shape* shape, const void* v_new, const void
 size_t gva_decode_step_workspace_bytes(const gva_shape* shape);
 
 /*
+ * gva_decode_step_noalloc - gva_decode_step without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). It allocates
+ * nothing: the split-K scratch is a fixed 4 MiB device array inside the
+ * library, one per device, held until the process ends (its address is
+ * looked up on the first call on each device, which also clears its arrival
+ * counters with one small kernel launch on `stream`).
+ *   Arguments and results as for gva_decode_step.
+ *   Limit: gva_decode_step_workspace_bytes(shape) <= 4 MiB and
+ *   B*G + B <= 512; a larger shape returns GVA_ERR_WORKSPACE before anything
+ *   is launched.
+ *   All calls on one device share the scratch array: calls that overlap in
+ *   time on one device (concurrent streams) race and give wrong results;
+ *   serialize them.
+ */
+gva_status gva_decode_step_noalloc(const gva_shape* shape, const void* v_new, const void* kr_new,
+                                   const void* q_nope, const void* q_rope, const void* M, void* v_cache,
+                                   void* kr_cache, int32_t* seq_lens, const int32_t* block_table, float scale,
+                                   float rope_base, void* out, hipStream_t stream);
+
+/*
  * Cache lifecycle on the paged cache (block_size == 64). The [gqa] page
  * (与位置编码和 KV Cache 的关系) lists what an engine does with cache blocks for
  * beam search, speculative decoding and prefix sharing: copy, share, commit
