@@ -63,7 +63,8 @@ def parse():
     p.add_argument("--profile-copy-mb", type=int, default=0,
                    help="with --profile-step/--profile-decode: first run a plain elementwise copy "
                         "(read N MiB, write N MiB) three times, the reference for traffic counters")
-    p.add_argument("--mode", choices=["step", "gqa", "folded", "multi", "lifecycle", "prefill", "ragged"],
+    p.add_argument("--mode", choices=["step", "gqa", "folded", "multi", "lifecycle", "prefill", "ragged",
+                                      "ceiling"],
                    default="step")
     return p.parse_args()
 
@@ -105,6 +106,9 @@ def main():
         return
     if args.mode == "ragged":
         ragged_bench(args)
+        return
+    if args.mode == "ceiling":
+        ceiling_bench(args)
         return
     wl = W.WORKLOADS[args.workload]
     if args.split >= 0:
@@ -343,9 +347,57 @@ def main():
         result["speedup_vs_gqa"] = cmp["time_ratio_gqa_over_gva"]
         result["gqa_byte_ratio"] = cmp["byte_ratio_gqa_over_gva"]
 
+    if use_graph:
+        # the same GPU's ceilings for this many bytes, measured in this process
+        ceil = measure_ceilings(mean_step_bytes)
+        result["ceiling"] = ceil
+        result["ceiling_GBps"] = ceil["read_GBps"]
+        result["frac_of_ceiling"] = round(achieved / ceil["read_GBps"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def measure_ceilings(read_bytes: int, replicas: int = 16):
+    """Ceilings on this GPU, graph-timed in this process (libgva_ceiling.so):
+    the per-launch floor of an empty kernel, a plain read of `read_bytes` in
+    the decode's load pattern (256 workgroups, 1 KB per load instruction,
+    `replicas` cold buffers), and a 2 GiB streaming read."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "compact_kv_cache_amd", "libgva_ceiling.so"))
+    lib.ceiling_empty_us.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.ceiling_read_us.argtypes = [ctypes.c_ulonglong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_double)]
+    us = ctypes.c_double()
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+        return us.value
+
+    wgs = 256
+    unit = wgs * 1024
+    rb = max(unit, (int(read_bytes) // unit) * unit)
+    empty = check(lib.ceiling_empty_us(100, ctypes.byref(us)), "empty-launch ceiling")
+    mid = check(lib.ceiling_read_us(rb, replicas, wgs, 64, ctypes.byref(us)), "read ceiling")
+    big_bytes = 2 << 30
+    big = check(lib.ceiling_read_us(big_bytes, 2, 2048, 20, ctypes.byref(us)), "2 GiB read ceiling")
+    return {"empty_launch_us": round(empty, 3),
+            "read_bytes": rb, "read_us": round(mid, 3), "read_GBps": round(rb / (mid * 1e-6) / 1e9, 1),
+            "read_2GiB_us": round(big, 2), "read_2GiB_GBps": round(big_bytes / (big * 1e-6) / 1e9, 1),
+            "kernel": "plain read, 1 KB per load instruction, 256 workgroups x 8 waves, "
+                      "every load of a wave requested at once; cold replicas; K launches in one graph"}
+
+
+def ceiling_bench(args):
+    """`--mode ceiling`: the ceilings alone (empty launch, plain read of the
+    mid cache's bytes, 2 GiB read), one JSON line."""
+    import workloads as W
+    wl = W.WORKLOADS["mid_bf16"]
+    bpt = (wl.G * wl.d_v + wl.d_r) * 2
+    res = measure_ceilings(wl.B * wl.S * bpt)
+    res["mode"] = "ceiling"
+    print(json.dumps(res), flush=True)
 
 
 KERNEL_SOURCES = ("compact_kv_cache_amd/csrc/decode_mfma.hip", "compact_kv_cache_amd/csrc/gva_device.hpp",
@@ -692,6 +744,15 @@ def ragged_bench(args):
         v, k, M, sl = reps[i % R]
         gva.gva_decode_step(shape, v_new, k_new, q, qr, M, v, k, sl, tab, wl.scale, wl.rope_base, out, ws)
 
+    if args.profile_decode or args.profile_step:  # eager launches only, for counter runs
+        for i in range(args.profile_decode):
+            dec(i)
+        for i in range(args.profile_step):
+            step(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "ragged", "profile_decode": args.profile_decode,
+                          "profile_step": args.profile_step, "replicas": R}))
+        return
     res = {"mode": "ragged",
            "config": {"workload": f"ragged_paged: B={wl.B} lengths U[{wl.len_lo}, {wl.len_hi}] (seeded, "
                                   f"mean {lens.mean():.0f}) H={wl.H} G={wl.G} d_r={wl.d_r} bf16, 64-token pages "

@@ -1,4 +1,5 @@
-"""Compile the HIP sources of the GVA library into libgva.so (gfx950).
+"""Compile the HIP sources of the GVA library into libgva.so (gfx950), and the
+benchmark's measurement kernels (bench_kernels/) into libgva_ceiling.so.
 
 Run as `python compact_kv_cache_amd/_build.py` or through
 `__graft_entry__.build()` (both load this file without importing the package,
@@ -52,6 +53,26 @@ def _compile(src: str) -> str:
     return obj
 
 
+BENCH_SRC = os.path.join(PKG, "bench_kernels")
+CEILING_LIB = os.path.join(PKG, "libgva_ceiling.so")
+
+
+def build_ceiling(verbose: bool = False) -> str:
+    """The benchmark's measurement kernels (empty launch, plain reads):
+    libgva_ceiling.so, separate from the GVA library."""
+    srcs = sorted(glob.glob(os.path.join(BENCH_SRC, "*.hip")))
+    objs = [_compile(src) for src in srcs]
+    tmp = CEILING_LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, CEILING_LIB)
+    if verbose:
+        print(f"built {CEILING_LIB}")
+    return CEILING_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
@@ -67,6 +88,7 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_ceiling(verbose)
     return LIB
 
 
