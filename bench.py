@@ -33,6 +33,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -446,6 +447,8 @@ def gqa_compare(args):
     res["config"] = {"workload": f"{wl.name}: B={wl.B} S={wl.S} H={wl.H} G={wl.G} d_v={wl.d_v} "
                                  f"d_r={wl.d_r} {wl.dtype}, contiguous caches, cold replicas",
                      "steps": args.steps}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_gqa(wl, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
@@ -691,6 +694,8 @@ def prefill_bench(args):
     res["roofline"] = {"bound": "mfma", "achieved": full["TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS,
                        "unit": "TFLOP/s", "frac": full["frac_bf16_peak"], "traffic": None,
                        "kernel": "prefill_mfma_kernel (whole prompt)"}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(wl, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
@@ -708,6 +713,7 @@ def ragged_bench(args):
     dev = torch.device("cuda:0")
     wl = W.WORKLOADS["ragged_paged"]
     K = args.steps
+    ROUNDS = 5
     lens = W.ragged_lens(wl)
     extra = K + 8
     table, nblk = W.paged_pool(lens + extra, 64, wl.seed)
@@ -757,29 +763,53 @@ def ragged_bench(args):
            "config": {"workload": f"ragged_paged: B={wl.B} lengths U[{wl.len_lo}, {wl.len_hi}] (seeded, "
                                   f"mean {lens.mean():.0f}) H={wl.H} G={wl.G} d_r={wl.d_r} bf16, 64-token pages "
                                   f"in a shuffled table, {R} cold replicas of the page pool", "steps": K,
-                      "split_tokens": gva.gva_decode_split_tokens(shape_at(n_max))}}
+                      "rounds": ROUNDS, "split_tokens": gva.gva_decode_split_tokens(shape_at(n_max))}}
+    lens0 = torch.tensor(lens.astype(np.int32), device=dev)
+
+    def reset_lengths():  # every round starts from the batch's own lengths
+        for r in reps:
+            r[3].copy_(lens0)
+        torch.cuda.synchronize()
+
+    graphs = {}
     for label, fn in (("decode", dec), ("fused_step", step)):
         for i in range(2 * R):
             fn(i)
-        torch.cuda.synchronize()
+        reset_lengths()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(K):
                 fn(i)
         torch.cuda.synchronize()
-        before = sum(int(r[3].sum()) for r in reps)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / K * 1e3
-        # cache tokens read per launch: every replica's current lengths (the step reads its new token too)
-        after = sum(int(r[3].sum()) for r in reps)
-        tokens = (before + after) / 2 / R if label == "fused_step" else before / R
-        nbytes = tokens * bpt
-        res[label] = {"us": round(us, 2), "cache_bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+        graphs[label] = g
+    # the two graphs replayed in turn, ROUNDS times each: the comparison is not
+    # at the mercy of one replay's clocks or of which graph runs first
+    times = {"decode": [], "fused_step": []}
+    tokens = {"decode": [], "fused_step": []}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(ROUNDS):
+        for label in ("decode", "fused_step"):
+            before = sum(int(r[3].sum()) for r in reps)
+            e0.record()
+            graphs[label].replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times[label].append(e0.elapsed_time(e1) / K * 1e3)
+            # cache tokens read per launch: every replica's lengths (the step reads its new token too)
+            after = sum(int(r[3].sum()) for r in reps)
+            tokens[label].append((before + after) / 2 / R)
+            reset_lengths()
+    for label in ("decode", "fused_step"):
+        us = statistics.median(times[label])
+        nbytes = statistics.mean(tokens[label]) * bpt
+        res[label] = {"us": round(us, 2), "us_each_round": [round(t, 2) for t in times[label]],
+                      "cache_bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
                       "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
+    pair = [s_ / d_ for s_, d_ in zip(times["fused_step"], times["decode"])]
+    res["step_over_decode"] = {"median": round(statistics.median(pair), 4),
+                               "each_round": [round(x, 4) for x in pair]}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_ragged(wl, lens, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
@@ -905,31 +935,115 @@ def measure_gva_vs_gqa(wl, K: int) -> dict:
             "byte_ratio_gqa_over_gva": round(out["gqa"]["bytes"] / out["gva"]["bytes"], 3)}
 
 
+def _oracle_reps(fn, seconds: float, max_reps: int = 1000):
+    """Call fn until `seconds` of wall time have passed (at least once)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= max_reps:
+            return reps, el
+
+
+def _oracle_threads() -> int:
+    from threadpoolctl import threadpool_info
+    return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+
+
 def cpu_baseline(wl, seconds: float):
     """The CPU oracle as it stands, on a bounded sample of the same workload:
     full decode steps (all B sequences, n = S + 1) repeated until `seconds`
     of CPU time have passed."""
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     import oracle as O
     import workloads as W
 
     inp = W.make_gva_inputs(wl, extra=1)
     n = np.full(wl.B, wl.S + 1)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        O.gva_decode_step(inp.V, inp.kr, inp.q_nope, inp.q_rope, inp.M, n, wl.scale,
-                          wl.rope_base, wl.dtype)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 1000:
-            break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(reps / el, 4), "unit": "steps/s", "cores": int(threads),
+    reps, el = _oracle_reps(lambda: O.gva_decode_step(inp.V, inp.kr, inp.q_nope, inp.q_rope, inp.M, n, wl.scale,
+                                                      wl.rope_base, wl.dtype), seconds)
+    return {"value": round(reps / el, 4), "unit": "steps/s", "cores": _oracle_threads(),
             "kind": "oracle",
             "sample": f"{reps} full oracle decode steps of {wl.name} (B={wl.B}, n={wl.S + 1}) "
                       f"in {el:.1f} s, float64 numpy, {len(os.sched_getaffinity(0))} cpus visible"}
+
+
+def cpu_baseline_gqa(wl, seconds: float, n_seq: int = 2):
+    """Oracle GVA decode and oracle GQA decode on the first `n_seq` sequences
+    of the workload (its full length S), each for about `seconds`, scaled to
+    whole-batch decodes per second."""
+    import dataclasses
+
+    import numpy as np
+
+    import oracle as O
+    import workloads as W
+
+    sub = dataclasses.replace(wl, B=n_seq)
+    inp = W.make_gva_inputs(sub)
+    n = np.full(n_seq, wl.S)
+    kr_rot = [O.append_positional_keys(k, 0, wl.rope_base, wl.dtype) for k in inp.kr]
+    q_rot = O.rope(inp.q_rope, (n - 1.0)[:, None], wl.rope_base)
+    r_gva, el_gva = _oracle_reps(lambda: O.gva_decode(inp.V, kr_rot, inp.q_nope, q_rot, inp.M, n, wl.scale),
+                                 seconds)
+    q, K, V = W.make_gqa_inputs(sub)
+    r_gqa, el_gqa = _oracle_reps(lambda: O.gqa_decode(q, K, V, n, wl.scale), seconds)
+    frac = n_seq / wl.B
+    return {"value": round(r_gva / el_gva * frac, 4), "unit": "decodes/s (whole batch)",
+            "gqa_value": round(r_gqa / el_gqa * frac, 4), "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"oracle gva_decode x{r_gva} in {el_gva:.1f} s and oracle gqa_decode x{r_gqa} in "
+                      f"{el_gqa:.1f} s on {n_seq} of the {wl.B} sequences (n={wl.S}), float64 numpy, "
+                      f"scaled by {n_seq}/{wl.B}"}
+
+
+def cpu_baseline_ragged(wl, lens, seconds: float, n_seq: int = 4):
+    """Oracle fused decode steps on the first `n_seq` sequences of the ragged
+    batch (their own lengths + the appended token), scaled to whole-batch
+    steps per second by their share of the batch's cache tokens."""
+    import dataclasses
+
+    import numpy as np
+
+    import oracle as O
+    import workloads as W
+
+    sub = dataclasses.replace(wl, B=n_seq)
+    inp = W.make_gva_inputs(sub, extra=1, lens=np.asarray(lens[:n_seq]))
+    n = np.asarray(lens[:n_seq]) + 1
+    reps, el = _oracle_reps(lambda: O.gva_decode_step(inp.V, inp.kr, inp.q_nope, inp.q_rope, inp.M, n, wl.scale,
+                                                      wl.rope_base, wl.dtype), seconds)
+    share = float(n.sum()) / float((np.asarray(lens) + 1).sum())
+    return {"value": round(reps / el * share, 4), "unit": "steps/s (whole batch)", "cores": _oracle_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} oracle fused steps of {n_seq} of the {wl.B} sequences (lengths "
+                      f"{', '.join(str(int(x)) for x in n)}) in {el:.1f} s, float64 numpy, scaled by their "
+                      f"share {share:.4f} of the batch's cache tokens"}
+
+
+def cpu_baseline_prefill(wl, seconds: float):
+    """Oracle causal prefill of one sequence's whole prompt (n = S queries over
+    S tokens), in algorithmic TFLOP/s (the causal count the GPU line uses)."""
+    import numpy as np
+
+    import oracle as O
+    import workloads as W
+
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 9))
+    n = wl.S
+    V = [W.round_storage(rng.standard_normal((wl.G, n, wl.d_v)), wl.dtype)]
+    kr = [O.append_positional_keys(W.round_storage(rng.standard_normal((n, wl.d_r)), wl.dtype), 0, wl.rope_base,
+                                   wl.dtype)]
+    q = W.round_storage(rng.standard_normal((1, n, wl.H, wl.d_n)), wl.dtype)
+    qr = W.round_storage(rng.standard_normal((1, n, wl.H, wl.d_r)), wl.dtype)
+    M = W.round_storage(rng.standard_normal((wl.H, wl.d_v, wl.d_n)) / 8, wl.dtype)
+    reps, el = _oracle_reps(lambda: O.gva_prefill(V, kr, q, qr, M, [n], wl.scale), seconds)
+    fl = prefill_flops(1, wl.H, n, n, wl.d_v, wl.d_r, wl.d_n, True)
+    return {"value": round(fl * reps / el / 1e12, 6), "unit": "TFLOP/s", "cores": _oracle_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} oracle prefills of one {n}-token prompt (all {n} queries, H={wl.H}) in {el:.1f} s, "
+                      f"float64 numpy; algorithmic causal flops as on the GPU line"}
 
 
 if __name__ == "__main__":

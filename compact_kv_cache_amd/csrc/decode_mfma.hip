@@ -231,7 +231,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     int64_t vbase = 0, kbase = 0;
     if constexpr (PAGED) {
       const int jb = min(t0 / kBlock, a.max_blocks - 1);
-      const int blk = a.block_table[(int64_t)b * a.max_blocks + jb];
+      const int blk = ld_table(a.block_table + (int64_t)b * a.max_blocks + jb);
       ok = ok && blk >= 0 && blk < a.num_blocks;
       vbase = ((int64_t)blk * G + g) * kBlock * kD;
       kbase = (int64_t)blk * kBlock * d_r;
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunc
     if (split == 0 && has_new && w == 0) {
       int64_t vrow = -1, krow = -1;
       if constexpr (PAGED) {
-        const int blk = a.block_table[(int64_t)b * a.max_blocks + pos / kBlock];
+        const int blk = ld_table(a.block_table + (int64_t)b * a.max_blocks + pos / kBlock);
         if (blk >= 0 && blk < a.num_blocks) {
           vrow = (((int64_t)blk * G + g) * kBlock + pos % kBlock) * kD;
           krow = ((int64_t)blk * kBlock + pos % kBlock) * d_r;

@@ -115,6 +115,16 @@ struct CacheGeom {
   const int32_t* block_table;  // null = contiguous
 };
 
+// Wave-uniform read of memory that no kernel writes while it runs (block
+// tables): the load goes through the scalar data cache. Through a plain
+// pointer the compiler must assume that a store earlier in the kernel (the
+// fused step's appended rows) may have changed the value, and issues a vector
+// load whose result the wave then waits for in full; the constant address
+// space states that nothing does.
+__device__ __forceinline__ int32_t ld_table(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
 // Pool block of token t of sequence b, or -1 if the table entry is invalid.
 __device__ __forceinline__ int page_of(const CacheGeom& c, int b, int t) {
   const int j = t / kBlock;
