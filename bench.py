@@ -45,6 +45,15 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X
 METRIC = "GVA decode steps/s + effective cache-read GB/s (% HBM peak), B=16 S=4096 bf16"
 
 
+def hold_device():
+    """Keep the GPU busy for about a millisecond (a spin kernel on the current
+    stream) while the host enqueues the timed region, so that the events
+    bracket the K steps as the device runs them back to back, not the host's
+    submission of the graph before its first kernel."""
+    import torch
+    torch.cuda._sleep(2_000_000)
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -224,6 +233,7 @@ def main():
                 fn(first + k)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hold_device()
         e0.record()
         g.replay()
         e1.record()
@@ -286,6 +296,7 @@ def main():
                 decode(k % R)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hold_device()
         e0.record()
         g2.replay()
         e1.record()

@@ -2,7 +2,8 @@
 // library): the per-launch floor of an empty kernel, and plain reads in the
 // decode's load pattern (every 16-byte load instruction of a wave covers 1 KB
 // of contiguous memory; non-temporal buffer loads), each timed as K launches
-// captured in one HIP graph and replayed between events on one stream.
+// captured in one HIP graph and replayed between events on one stream (behind
+// a short spin kernel, so the host's submission of the graph is not timed).
 //
 //   ceiling_empty_us(launches, &us)             empty kernel, 256 x 512 threads
 //   ceiling_read_us(bytes, replicas, wgs, launches, &us)
@@ -24,6 +25,14 @@ constexpr int kWord3 = 0x00020000;
 constexpr int kNonTemporal = 2;
 
 __global__ void empty_kernel() {}
+
+// One wave that returns once `ticks` of the 100 MHz real-time counter have
+// passed: keeps the device busy while the host enqueues a timed graph.
+__global__ void spin_kernel(unsigned long long ticks) {
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) {
+  }
+}
 
 // All of a wave's loads requested at once (NPW <= 17 per wave).
 template <int NPW>
@@ -81,7 +90,11 @@ hipError_t graph_time(hipStream_t s, int launches, F launch, double* us) {
   if (e == hipSuccess) e = hipEventCreate(&e1);
   float best = 1e30f;
   for (int rep = 0; rep < 3 && e == hipSuccess; ++rep) {
-    e = hipEventRecord(e0, s);
+    // the device spins for 1 ms while the host enqueues the replay, so the
+    // events bracket the launches as the device runs them back to back
+    spin_kernel<<<1, 64, 0, s>>>(100000ull);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipEventRecord(e0, s);
     if (e == hipSuccess) e = hipGraphLaunch(ge, s);
     if (e == hipSuccess) e = hipEventRecord(e1, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
