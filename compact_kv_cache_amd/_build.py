@@ -27,8 +27,13 @@ ARCH = os.environ.get("GVA_OFFLOAD_ARCH", "gfx950")
 # The atomic optimizer is off: every atomic here is issued by one lane, and its
 # wave-aggregated rewrite reads the result back at once, which makes the wave
 # wait for all of its earlier loads (the tile stream) right after the atomic.
+# Kernel-argument preloading: the leading scalar arguments of a kernel (up to
+# 14 dwords beside the argument pointer) arrive in scalar registers at wave
+# launch instead of through a memory fetch; code objects keep a fallback entry
+# that loads them for firmware without the feature.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
+                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+                "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Wall",
           "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 

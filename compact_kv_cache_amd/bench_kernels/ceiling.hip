@@ -102,10 +102,10 @@ hipError_t graph_time(hipStream_t s, int launches, F launch, double* us) {
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
     if (e == hipSuccess && ms < best) best = ms;
   }
-  if (e0) hipEventDestroy(e0);
-  if (e1) hipEventDestroy(e1);
-  if (ge) hipGraphExecDestroy(ge);
-  if (g) hipGraphDestroy(g);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (ge) (void)hipGraphExecDestroy(ge);
+  if (g) (void)hipGraphDestroy(g);
   if (e == hipSuccess) *us = best * 1e3 / launches;
   return e;
 }
@@ -119,7 +119,7 @@ int ceiling_empty_us(int launches, double* us) {
   hipError_t e = hipStreamCreate(&s);
   if (e != hipSuccess) return e;
   e = graph_time(s, launches, [&](int) { empty_kernel<<<256, 512, 0, s>>>(); }, us);
-  hipStreamDestroy(s);
+  (void)hipStreamDestroy(s);
   return e;
 }
 
@@ -146,9 +146,9 @@ int ceiling_read_us(unsigned long long bytes, int replicas, int wgs, int launche
         read_ring_kernel<<<wgs, 512, 0, s>>>(src, pw, sink);
     }, us);
   }
-  if (s) hipStreamDestroy(s);
-  if (sink) hipFree(sink);
-  if (buf) hipFree(buf);
+  if (s) (void)hipStreamDestroy(s);
+  if (sink) (void)hipFree(sink);
+  if (buf) (void)hipFree(buf);
   return e;
 }
 

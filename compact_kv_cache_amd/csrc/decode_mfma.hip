@@ -89,8 +89,31 @@ struct Frags {
 };
 
 
+// The arguments that the first loads depend on come first, as scalars: gfx950
+// preloads leading kernel arguments (14 dwords here) into scalar registers at
+// wave launch, so the map, query and first tile requests wait for no
+// kernel-argument fetch (a by-value struct is never preloaded). The launch
+// struct repeats them; the copies below take precedence. H and d_r follow
+// from the template (H = HPG * G, d_r = 8 * KR).
 template <int HPG, bool PAGED, int KR, bool GQA, bool STEP, int NQ>
-__global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(DecodeLaunch a) {
+__global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void* arg_v_cache, const void* arg_kr_cache,
+                                                                      const void* arg_M, const void* arg_q_nope,
+                                                                      int arg_B, int arg_G, int arg_split,
+                                                                      int arg_n_split, int arg_max_seq_len,
+                                                                      int arg_capacity, DecodeLaunch launch) {
+  DecodeLaunch a = launch;
+  a.v_cache = arg_v_cache;
+  a.kr_cache = arg_kr_cache;
+  a.M = arg_M;
+  a.q_nope = arg_q_nope;
+  a.B = arg_B;
+  a.G = arg_G;
+  a.split = arg_split;
+  a.n_split = arg_n_split;
+  a.max_seq_len = arg_max_seq_len;
+  a.capacity = arg_capacity;
+  a.H = HPG * arg_G;
+  a.d_r = 8 * KR;
   constexpr bool DR = KR > 0;  // positional slice present (d_r = 8 * KR)
   // NQ queries per sequence (the last NQ cached tokens, each reading the cache
   // up to its own position); the matrix-core column col carries query
@@ -656,9 +679,11 @@ hipError_t mfma_launch(const DecodeLaunch& a, hipStream_t s) {
   const int pairs = a.B * a.n_split;
   const dim3 grid(((pairs + 7) / 8) * 8 * a.G);
   if (a.paged)
-    decode_mfma_kernel<HPG, true, KR, GQA, STEP, NQ><<<grid, 64 * kWaves, 0, s>>>(a);
+    decode_mfma_kernel<HPG, true, KR, GQA, STEP, NQ><<<grid, 64 * kWaves, 0, s>>>(
+        a.v_cache, a.kr_cache, a.M, a.q_nope, a.B, a.G, a.split, a.n_split, a.max_seq_len, a.capacity, a);
   else
-    decode_mfma_kernel<HPG, false, KR, GQA, STEP, NQ><<<grid, 64 * kWaves, 0, s>>>(a);
+    decode_mfma_kernel<HPG, false, KR, GQA, STEP, NQ><<<grid, 64 * kWaves, 0, s>>>(
+        a.v_cache, a.kr_cache, a.M, a.q_nope, a.B, a.G, a.split, a.n_split, a.max_seq_len, a.capacity, a);
   return hipGetLastError();
 }
 
