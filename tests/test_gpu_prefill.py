@@ -147,7 +147,9 @@ def test_prefill_agrees_with_multi_query_decode(nq):
 def test_prefill_mid_size_sampled():
     """The prefill workload's shape (B=16, a 4096-token prompt, all 4096 tokens
     as queries), in the launch configuration of the benchmark, against the
-    oracle on sampled (sequence, query) rows computed one by one."""
+    oracle: every query of two whole sequences (the oracle's causal prefill),
+    and sampled (sequence, query) rows of the others computed one by one with
+    the decode oracle."""
     wl = W.WORKLOADS["mid_bf16"]
     n = 4096
     lens = np.full(16, n)
@@ -168,6 +170,10 @@ def test_prefill_mid_size_sampled():
         q_rot = O.rope(qr[b, j], float(j), BASE)
         ref = O.gva_decode_seq(inp.V[b], kr_rot, qn[b, j], q_rot, inp.M, j + 1, wl.scale)
         S.assert_close(got[b, j], ref, "bf16", f"prefill mid b={b} j={j}")
+    for b in (5, 14):
+        ref = O.gva_prefill_step([inp.V[b]], [inp.kr[b]], qn[b:b + 1], qr[b:b + 1], inp.M, [n], wl.scale, BASE,
+                                 "bf16")
+        S.assert_close(got[b:b + 1], ref, "bf16", f"prefill mid, every query of b={b}")
 
 
 def test_prefill_empty_and_validation():
