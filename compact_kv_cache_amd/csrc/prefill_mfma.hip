@@ -23,9 +23,11 @@
 // to one of two LDS buffers while the other is computed, and read by every
 // wave. (Measured at the mid shape: 4 waves x 4 blocks ran 1.29x faster than
 // 8 waves x 2 blocks.) Per wave and tile, on the matrix cores:
-//   scores  S^T[tok][col] = V[tok] . q'[col] + k_r[tok] . q_rope[col] (A = V
-//           rows from LDS, B = the column block's queries), 8 MFMAs of
-//           16x16x32 per block, and 4 of 16x16x16 for d_r <= 16 (else 16x16x32);
+//   scores  S^T[tok][col] = V[tok] . q'[col] + k_r[tok] . q_rope[col] - m_ref
+//           (A = V rows from LDS, B = the column block's queries), 12 MFMAs of
+//           16x16x32 per block: two for the content part and one for the
+//           positional slice, whose spare channel carries the reference shift
+//           (d_r <= 24);
 //   mask    tokens past a column's own position (tiles on the diagonal only);
 //   softmax online per column, the max over the wave's four 16-lane rows with
 //           the row-swap permutes;
@@ -45,17 +47,6 @@ namespace {
 
 constexpr int kPWaves = 4;           // waves per workgroup
 constexpr float kRescaleLog2P = 8.f; // move the reference max only beyond 2^8
-
-// 4-element operand of v_mfma_f32_16x16x16_bf16 (lane: row or column
-// lane%16, k = 4*(lane/16) .. +3)
-union Frag4 {
-  i16x4 s;
-  uint2 u;
-  __bf16 h[4];
-};
-__device__ __forceinline__ f32x4 mma16(const Frag4& a, const Frag4& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.s, b.s, c, 0, 0, 0);
-}
 
 // 16-column blocks per wave: 4 where the state fits the 256 registers of a
 // wave at two waves per SIMD without spilling, else 3.
@@ -99,11 +90,16 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
   // ---- the wave's column blocks: absorbed queries as B operands ---------------
   const __bf16* qn = reinterpret_cast<const __bf16*>(a.q_nope);
   const __bf16* qrp = reinterpret_cast<const __bf16*>(a.q_rope);
-  // Positional slice: d_r <= 16 fits one K = 16 product (4 channels per
-  // lane), wider slices take the K = 32 product like the content part.
-  constexpr bool K16 = DR && KR <= 2;
-  Frag qb[kCB][2], qr[K16 ? 1 : kCB];
-  Frag4 qr4[K16 ? kCB : 1];
+  // Positional slice: one K = 32 product. Where d_r <= 24 its spare channel
+  // k = d_r carries the reference shift (SK): the key side holds 1 there and
+  // the query side -m_ref, rounded to bf16 (the reference is kept
+  // bf16-representable), so the scores leave the matrix cores already
+  // shifted, with no accumulator start to broadcast per tile. (An earlier form
+  // took d_r <= 16 as a separate K = 16 product added per score: hipcc issued
+  // a K = 16 and a K = 32 product chained through one accumulator back to
+  // back without wait states, which summed wrongly on the GPU.)
+  constexpr bool SK = KR >= 1 && KR <= 3;
+  Frag qb[kCB][2], qr[DR ? kCB : 1];
   int wave_pmin = INT32_MAX, wave_pmax = -1;  // over the wave's columns (uniform)
 #pragma unroll
   for (int u = 0; u < kCB; ++u) {
@@ -146,13 +142,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
 #pragma unroll
         for (int e = 0; e < 8; ++e) qb[u][kc].h[e] = (__bf16)((float)q_in[kc].h[e] * sl2);
     }
-    if constexpr (K16) {
-      Frag4 x;
-      x.u = *reinterpret_cast<const uint2*>(qrp + qrow * d_r + 4 * min(r, 2 * KR - 1));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qr4[u].h[e] = (__bf16)((float)x.h[e] * sl2);
-      if (4 * r >= d_r || !jv) qr4[u].u = uint2{0u, 0u};
-    } else if constexpr (DR) {
+    if constexpr (DR) {
       Frag x;
       x.u = ld16(qrp + qrow * d_r, kr_off);
 #pragma unroll
@@ -161,15 +151,26 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
     }
     if (!jv) {
       qb[u][0].u = qb[u][1].u = u32x4{0u, 0u, 0u, 0u};
-      if constexpr (!K16) qr[u].u = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (DR) qr[u].u = u32x4{0u, 0u, 0u, 0u};
     }
   }
 
   // ---- key tiles: cooperative loads into two LDS buffers ------------------------
   // Stage layout per buffer as in the decode: 64 V rows of 128 bytes with
   // their 16-byte chunks XOR-swizzled per row, then the positional-key rows.
-  constexpr int kStage = 8192 + 1024 * (KR > 0 ? KR : 0);
+  constexpr int kOnesOff = 8192 + 1024 * (KR > 0 ? KR : 0);  // SK: the key side's shift channel
+  constexpr int kStage = kOnesOff + (SK ? 3 * 256 * KR + 16 : 0);
   __shared__ __attribute__((aligned(16))) char stage[2][kStage];
+  if constexpr (SK) {
+    // one 16-byte chunk [1, 0, ..., 0] per 16-token sub-tile, at the sub-tile
+    // stride of the positional-key rows, in both buffers (never overwritten)
+    if (tid < 8) {
+      Frag one;
+      one.u = u32x4{0u, 0u, 0u, 0u};
+      one.h[0] = (__bf16)1.f;
+      *reinterpret_cast<u32x4*>(&stage[tid >> 2][kOnesOff + (tid & 3) * 256 * KR]) = one.u;
+    }
+  }
   // V: 16-byte chunk c = t + 64*kPWaves*i of the tile (row c/8, chunk c%8)
   constexpr int kNV = 512 / (64 * kPWaves);  // V chunks per thread
   const int vch = tid & 7;
@@ -232,9 +233,10 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
 
   // Scores come out of the matrix cores in log2 units (the queries carry
   // scale*log2(e)) and already shifted by the column's reference max m_ref
-  // (the accumulator starts at -m_ref), so p = 2^s with no further
-  // arithmetic. m_ref is set by the column's first tile and moves only when
-  // a tile's shifted max exceeds 2^8; p stays below 256.
+  // (through the positional product's shift channel, or the accumulator
+  // start where there is none), so p = 2^s with no further arithmetic. m_ref
+  // is set by the column's first tile and moves only when a tile's shifted
+  // max exceeds 2^8 (p stays below about 256).
   f32x4 acc[kCB][4];
   float m_ref[kCB], l_run[kCB];
 #pragma unroll
@@ -247,16 +249,16 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
 
   auto compute = [&](const char* st_base, int t0) {
     if (t0 > wave_pmax) return;  // every query of the wave is before this tile (uniform)
-    Frag sa[4][2], kr[K16 ? 1 : 4];
-    Frag4 kr4[K16 ? 4 : 1];
+    Frag sa[4][2], kr[DR ? 4 : 1];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int row = 16 * st + col;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
         sa[st][hh].u = *reinterpret_cast<const u32x4*>(st_base + row * (kD * 2) + 16 * ((4 * hh + r) ^ stage_swizzle(row)));
-      if constexpr (K16)
-        kr4[st].u = *reinterpret_cast<const uint2*>(st_base + 8192 + row * (16 * KR) + 8 * min(r, 2 * KR - 1));
+      if constexpr (SK)
+        kr[st].u = *reinterpret_cast<const u32x4*>(
+            st_base + (r == KR ? kOnesOff + st * 256 * KR : 8192 + row * (16 * KR) + 2 * kr_off));
       else if constexpr (DR)
         kr[st].u = *reinterpret_cast<const u32x4*>(st_base + 8192 + row * (16 * KR) + 2 * kr_off);
     }
@@ -266,13 +268,15 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
       f32x4 s[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const float c0 = m_ref[u] == -INFINITY ? 0.f : -m_ref[u];
-        f32x4 c = mma(sa[st][0], qb[u][0], f32x4{c0, c0, c0, c0});
+        f32x4 c;
+        if constexpr (SK) {
+          c = mma(sa[st][0], qb[u][0], kZero4);
+        } else {
+          const float c0 = m_ref[u] == -INFINITY ? 0.f : -m_ref[u];
+          c = mma(sa[st][0], qb[u][0], f32x4{c0, c0, c0, c0});
+        }
         c = mma(sa[st][1], qb[u][1], c);
-        if constexpr (K16)  // own accumulator: chained after (or before) the K = 32 products
-          c += mma16(kr4[st], qr4[u], kZero4);  // through one accumulator it gave wrong sums
-        else if constexpr (DR)
-          c = mma(kr[st], qr[u], c);
+        if constexpr (DR) c = mma(kr[st], qr[u], c);
         s[st] = c;
       }
       // causal mask on the diagonal tiles: token past the column's position
@@ -295,15 +299,34 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
       // shift of the reference: the whole max on a column's first tile,
       // else only beyond 2^8; none for a column whose scores are all masked
       const bool unset = m_ref[u] == -INFINITY;
-      const float shift = (mx == -INFINITY) ? 0.f : (unset || mx > kRescaleLog2P) ? mx : 0.f;
-      if (__any(shift != 0.f)) {
-        const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-shift);  // unset: nothing accumulated
-        l_run[u] *= alpha;
+      if constexpr (SK) {
+        // move the (bf16-representable) reference: the whole max on a
+        // column's first tile, else only beyond 2^8; none for a column
+        // whose scores are all masked
+        const bool move = mx != -INFINITY && (unset || mx > kRescaleLog2P);
+        if (__any(move)) {
+          const float m_new = move ? (float)(__bf16)(unset ? mx : m_ref[u] + mx) : m_ref[u];
+          const float shift = move ? (unset ? m_new : m_new - m_ref[u]) : 0.f;
+          const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-shift);  // unset: nothing accumulated
+          l_run[u] *= alpha;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) acc[u][db] *= alpha;
-        m_ref[u] = unset ? (mx == -INFINITY ? m_ref[u] : mx) : m_ref[u] + shift;
+          for (int db = 0; db < 4; ++db) acc[u][db] *= alpha;
+          m_ref[u] = m_new;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) s[st] -= shift;
+          for (int st = 0; st < 4; ++st) s[st] -= shift;
+          if (r == KR) qr[u].h[0] = (__bf16)(m_ref[u] == -INFINITY ? 0.f : -m_ref[u]);
+        }
+      } else {  // d_r = 0 or 32: the shift rides in the accumulator start
+        const float shift = (mx == -INFINITY) ? 0.f : (unset || mx > kRescaleLog2P) ? mx : 0.f;
+        if (__any(shift != 0.f)) {
+          const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-shift);  // unset: nothing accumulated
+          l_run[u] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) acc[u][db] *= alpha;
+          m_ref[u] = unset ? (mx == -INFINITY ? m_ref[u] : mx) : m_ref[u] + shift;
+#pragma unroll
+          for (int st = 0; st < 4; ++st) s[st] -= shift;
+        }
       }
       float psum = 0.f;
 #pragma unroll
