@@ -68,7 +68,7 @@ typedef enum gva_dtype {
  * Problem description shared by all calls.
  *   B, H, G          sequences, query heads, value groups (H % G == 0,
  *                    H/G in {1, 2, 4})
- *   d_n, d_v         content-query and value widths (this build: 64, 64)
+ *   d_n, d_v         content-query and value widths (the kernels take 64, 64)
  *   d_r              shared positional-key width (0, 8, 16, 24 or 32)
  *   capacity         contiguous cache: token slots per sequence;
  *                    paged cache: ignored
