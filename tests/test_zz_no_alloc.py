@@ -70,3 +70,51 @@ def test_noalloc_refuses_a_shape_beyond_its_scratch():
     with pytest.raises(gva.GvaError, match="GVA_ERR_WORKSPACE"):
         gva.gva_decode_step_noalloc(shape, z(B, 4, 64), z(B, 16), z(B, 16, 64), z(B, 16, 16), z(16, 64, 64),
                                     z(1, 4, 64, 64), z(1, 64, 16), lens, table, 0.1, BASE, z(B, 16, 64))
+
+
+def test_noalloc_step_under_graph_capture():
+    """The callers this entry point is for capture it: three allocation-free
+    fused steps captured in one graph, replayed three times with eager work
+    between the replays, equal nine eager steps through gva_decode_step with a
+    caller workspace on an identical cache, bit for bit after every replay."""
+    wl = W.Workload("noalloc_graph", 9, B=3, H=16, G=4, d_n=64, d_v=64, d_r=16, S=0, dtype="bf16")
+    lens = np.array([500, 1030, 77])
+    inp = W.make_gva_inputs(wl, lens=lens, extra=10, seed=103)
+    cap = 1100
+    ca, cb = (GvaCache(3, 16, 4, 64, 64, 16, dtype="bf16", capacity=cap) for _ in range(2))
+    for c in (ca, cb):
+        for b, n in enumerate(lens):
+            c.append_one(b, S.dev(inp.V[b][:, :n], "bf16"), S.dev(inp.kr[b][:n], "bf16"), BASE)
+    qn, qr, Md = (S.dev(x, "bf16") for x in (inp.q_nope, inp.q_rope, inp.M))
+    news = [(S.dev(np.stack([inp.V[b][:, n + i] for b, n in enumerate(lens)]), "bf16"),
+             S.dev(np.stack([inp.kr[b][n + i] for b, n in enumerate(lens)]), "bf16")) for i in range(4)]
+    split = 128
+    shape = ca.shape(cap, split)
+    out_a = torch.empty(3, 16, 64, dtype=torch.bfloat16, device="cuda")
+    out_b = torch.empty_like(out_a)
+    ws_b = cb.step_workspace(cap, split)
+    print("[case] noalloc graph capture", flush=True)
+    # one eager call on each side first (the scratch is set up outside capture)
+    v0, k0 = news[0]
+    gva.gva_decode_step_noalloc(shape, v0, k0, qn, qr, Md, ca.v_cache, ca.kr_cache, ca.seq_lens, None, wl.scale,
+                                BASE, out_a)
+    cb.step(v0, k0, qn, qr, Md, wl.scale, out_b, cap, split, workspace=ws_b)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for v1, k1 in news[1:]:
+            gva.gva_decode_step_noalloc(shape, v1, k1, qn, qr, Md, ca.v_cache, ca.kr_cache, ca.seq_lens, None,
+                                        wl.scale, BASE, out_a)
+    torch.cuda.synchronize()
+    assert ca.seq_lens.cpu().tolist() == (lens + 1).tolist()  # capture runs nothing
+    for rep in range(3):
+        print(f"[case] noalloc graph replay {rep}", flush=True)
+        g.replay()
+        for v1, k1 in news[1:]:
+            cb.step(v1, k1, qn, qr, Md, wl.scale, out_b, cap, split, workspace=ws_b)
+        torch.cuda.synchronize()
+        assert torch.equal(ca.seq_lens, cb.seq_lens), rep
+        assert torch.equal(out_a, out_b), rep
+        assert torch.equal(ca.v_cache, cb.v_cache) and torch.equal(ca.kr_cache, cb.kr_cache), rep
+    assert ca.seq_lens.cpu().tolist() == (lens + 10).tolist()
