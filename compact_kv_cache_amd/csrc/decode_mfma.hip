@@ -538,14 +538,17 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
           if (tok >= t_end || (NQ > 1 && tok > p_col)) s[st][i] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    float lmx = -INFINITY;  // over this lane's 16 scores of the column
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[st][i]);
-    mx = rows_max(mx);
-    const float m_new = (mx > m_ref + thr) ? mx : m_ref;
-    if (__any(m_new != m_ref)) {
+      for (int i = 0; i < 4; ++i) lmx = fmaxf(lmx, s[st][i]);
+    // The reference moves only where the column max passes it by thr; a
+    // lane's own max decides whether that can happen anywhere in the wave,
+    // and only then is the column max formed across the four lanes.
+    if (__any(lmx > m_ref + thr)) {
+      const float mx = rows_max(lmx);
+      const float m_new = (mx > m_ref + thr) ? mx : m_ref;
       // 0 on a column's first tile; 1 where the max does not move (also a
       // column that has seen only masked scores so far)
       const float alpha = (m_new == m_ref) ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * sl2);

@@ -290,42 +290,46 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
           for (int i = 0; i < 4; ++i)
             if (t0 + 16 * st + 4 * r + i > pcol) s[st][i] = -INFINITY;
       }
-      float mx = -INFINITY;
+      float lmx = -INFINITY;  // over this lane's 16 scores of the column
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[st][i]);
-      mx = rows_max(mx);
+        for (int i = 0; i < 4; ++i) lmx = fmaxf(lmx, s[st][i]);
       // shift of the reference: the whole max on a column's first tile,
-      // else only beyond 2^8; none for a column whose scores are all masked
+      // else only beyond 2^8; none for a column whose scores are all masked.
+      // A lane's own max decides whether any column of the wave may need it;
+      // only then is the column max formed across the four lanes.
       const bool unset = m_ref[u] == -INFINITY;
-      if constexpr (SK) {
-        // move the (bf16-representable) reference: the whole max on a
-        // column's first tile, else only beyond 2^8; none for a column
-        // whose scores are all masked
-        const bool move = mx != -INFINITY && (unset || mx > kRescaleLog2P);
-        if (__any(move)) {
-          const float m_new = move ? (float)(__bf16)(unset ? mx : m_ref[u] + mx) : m_ref[u];
-          const float shift = move ? (unset ? m_new : m_new - m_ref[u]) : 0.f;
-          const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-shift);  // unset: nothing accumulated
-          l_run[u] *= alpha;
+      if (__any(lmx > kRescaleLog2P || (unset && lmx != -INFINITY))) {
+        const float mx = rows_max(lmx);
+        if constexpr (SK) {
+          // move the (bf16-representable) reference: the whole max on a
+          // column's first tile, else only beyond 2^8; none for a column
+          // whose scores are all masked
+          const bool move = mx != -INFINITY && (unset || mx > kRescaleLog2P);
+          if (__any(move)) {
+            const float m_new = move ? (float)(__bf16)(unset ? mx : m_ref[u] + mx) : m_ref[u];
+            const float shift = move ? (unset ? m_new : m_new - m_ref[u]) : 0.f;
+            const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-shift);  // unset: nothing accumulated
+            l_run[u] *= alpha;
 #pragma unroll
-          for (int db = 0; db < 4; ++db) acc[u][db] *= alpha;
-          m_ref[u] = m_new;
+            for (int db = 0; db < 4; ++db) acc[u][db] *= alpha;
+            m_ref[u] = m_new;
 #pragma unroll
-          for (int st = 0; st < 4; ++st) s[st] -= shift;
-          if (r == KR) qr[u].h[0] = (__bf16)(m_ref[u] == -INFINITY ? 0.f : -m_ref[u]);
-        }
-      } else {  // d_r = 0 or 32: the shift rides in the accumulator start
-        const float shift = (mx == -INFINITY) ? 0.f : (unset || mx > kRescaleLog2P) ? mx : 0.f;
-        if (__any(shift != 0.f)) {
-          const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-shift);  // unset: nothing accumulated
-          l_run[u] *= alpha;
+            for (int st = 0; st < 4; ++st) s[st] -= shift;
+            if (r == KR) qr[u].h[0] = (__bf16)(m_ref[u] == -INFINITY ? 0.f : -m_ref[u]);
+          }
+        } else {  // d_r = 0 or 32: the shift rides in the accumulator start
+          const float shift = (mx == -INFINITY) ? 0.f : (unset || mx > kRescaleLog2P) ? mx : 0.f;
+          if (__any(shift != 0.f)) {
+            const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-shift);  // unset: nothing accumulated
+            l_run[u] *= alpha;
 #pragma unroll
-          for (int db = 0; db < 4; ++db) acc[u][db] *= alpha;
-          m_ref[u] = unset ? (mx == -INFINITY ? m_ref[u] : mx) : m_ref[u] + shift;
+            for (int db = 0; db < 4; ++db) acc[u][db] *= alpha;
+            m_ref[u] = unset ? (mx == -INFINITY ? m_ref[u] : mx) : m_ref[u] + shift;
 #pragma unroll
-          for (int st = 0; st < 4; ++st) s[st] -= shift;
+            for (int st = 0; st < 4; ++st) s[st] -= shift;
+          }
         }
       }
       float psum = 0.f;
