@@ -558,14 +558,13 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
       m_ref = m_new;
     }
     const float bias = (m_ref == -INFINITY) ? 0.f : -m_ref * sl2;  // all-masked column: p = 0
-    float psum = 0.f;
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[st][i] = __builtin_amdgcn_exp2f(fmaf(s[st][i], sl2, bias));
-        psum += s[st][i];
-      }
+      for (int i = 0; i < 4; ++i) s[st][i] = __builtin_amdgcn_exp2f(fmaf(s[st][i], sl2, bias));
+    float psum = s[0][0];  // (not 0 + ...: the compiler keeps an add of +0)
+#pragma unroll
+    for (int e = 1; e < 16; ++e) psum += s[e >> 2][e & 3];
     l_run += psum;
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {

@@ -332,14 +332,13 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
           }
         }
       }
-      float psum = 0.f;
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s[st][i] = __builtin_amdgcn_exp2f(s[st][i]);
-          psum += s[st][i];
-        }
+        for (int i = 0; i < 4; ++i) s[st][i] = __builtin_amdgcn_exp2f(s[st][i]);
+      float psum = s[0][0];  // (not 0 + ...: the compiler keeps an add of +0)
+#pragma unroll
+      for (int e = 1; e < 16; ++e) psum += s[e >> 2][e & 3];
       l_run[u] += psum;
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr)
