@@ -357,6 +357,7 @@ def main():
         "decode_cache_read_GBps": round(dec_gbps, 1),
         "decode_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
         "decode_event_per_call_us": round(dec_ms_mean * 1e3, 3),
+        "decode_event_per_call_median_us": round(float(np.median(dec_ms)) * 1e3, 3),
         "eager_ms_per_step": round(ms_eager, 6),
         "three_call_steps_per_s": None if ms_three is None else round(1e3 / ms_three, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
