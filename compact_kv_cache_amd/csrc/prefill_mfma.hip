@@ -85,6 +85,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
   const int p_last = first + min(q0 + QW, nq) - 1;
   const int n_tiles = p_last >= 0 ? p_last / kTile + 1 : 0;
   const float sl2 = a.scale * kLog2e;
+  const float thr = kRescaleLog2P / sl2;  // the reference moves past this (raw score units)
   const int kr_off = DR ? 8 * min(r, KR - 1) : 0;  // lanes past d_r re-read a valid slice
 
   // ---- the wave's column blocks: absorbed queries as B operands ---------------
@@ -119,8 +120,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
     if (a.M != nullptr) {  // uniform
       // q'^T = M_h q^T: A = rows of M_h in the permuted order that lands the
       // product in the B layout (lane (col, r) gets q'[32*kc + 8r + e] in
-      // D[2kc + e/4][e%4]); accumulated in fp32, scaled by scale*log2(e) and
-      // rounded to bf16 once.
+      // D[2kc + e/4][e%4]); accumulated in fp32 and rounded to bf16 once.
       const __bf16* Mh = reinterpret_cast<const __bf16*>(a.M) + (int64_t)h * kD * kD;
       f32x4 D[4];
 #pragma unroll
@@ -135,18 +135,15 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qb[u][kc].h[e] = (__bf16)(D[2 * kc + (e >> 2)][e & 3] * sl2);
+        for (int e = 0; e < 8; ++e) qb[u][kc].h[e] = (__bf16)D[2 * kc + (e >> 2)][e & 3];
     } else {  // q_nope already holds q' (the maps folded into the projection)
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qb[u][kc].h[e] = (__bf16)((float)q_in[kc].h[e] * sl2);
+      for (int kc = 0; kc < 2; ++kc) qb[u][kc].u = q_in[kc].u;
     }
     if constexpr (DR) {
       Frag x;
       x.u = ld16(qrp + qrow * d_r, kr_off);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qr[u].h[e] = (__bf16)((float)x.h[e] * sl2);
+      qr[u].u = x.u;  // as given: a scaled copy would add a rounding the scores do not need
       if (8 * r >= d_r) qr[u].u = u32x4{0u, 0u, 0u, 0u};
     }
     if (!jv) {
@@ -231,12 +228,17 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
     tr_off0 = row * (kD * 2) + 16 * (((col & 3) >> 1) ^ stage_swizzle(row)) + 8 * (col & 1);
   }
 
-  // Scores come out of the matrix cores in log2 units (the queries carry
-  // scale*log2(e)) and already shifted by the column's reference max m_ref
-  // (through the positional product's shift channel, or the accumulator
-  // start where there is none), so p = 2^s with no further arithmetic. m_ref
-  // is set by the column's first tile and moves only when a tile's shifted
-  // max exceeds 2^8 (p stays below about 256).
+  // Scores come out of the matrix cores in raw units (q . k, the queries as
+  // rounded once: q' = M q to bf16, the positional slice as given) and
+  // already shifted by the column's reference max m_ref (through the
+  // positional product's shift channel, or the accumulator start where there
+  // is none), so p = 2^(scale*log2(e)*s) takes one multiply before the
+  // exponential. m_ref is set by the column's first tile and moves only when
+  // a tile's shifted max exceeds thr = 8 / (scale*log2(e)) (p stays below
+  // about 2^8). (Folding scale*log2(e) into the queries before their bf16
+  // rounding would save the multiply, but it rounds the positional slice a
+  // second time: a relative error of 2^-9 in scores that can reach tens of
+  // log2 units.)
   f32x4 acc[kCB][4];
   float m_ref[kCB], l_run[kCB];
 #pragma unroll
@@ -300,17 +302,17 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
       // A lane's own max decides whether any column of the wave may need it;
       // only then is the column max formed across the four lanes.
       const bool unset = m_ref[u] == -INFINITY;
-      if (__any(lmx > kRescaleLog2P || (unset && lmx != -INFINITY))) {
+      if (__any(lmx > thr || (unset && lmx != -INFINITY))) {
         const float mx = rows_max(lmx);
         if constexpr (SK) {
           // move the (bf16-representable) reference: the whole max on a
           // column's first tile, else only beyond 2^8; none for a column
           // whose scores are all masked
-          const bool move = mx != -INFINITY && (unset || mx > kRescaleLog2P);
+          const bool move = mx != -INFINITY && (unset || mx > thr);
           if (__any(move)) {
             const float m_new = move ? (float)(__bf16)(unset ? mx : m_ref[u] + mx) : m_ref[u];
             const float shift = move ? (unset ? m_new : m_new - m_ref[u]) : 0.f;
-            const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-shift);  // unset: nothing accumulated
+            const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-shift * sl2);  // unset: nothing accumulated
             l_run[u] *= alpha;
 #pragma unroll
             for (int db = 0; db < 4; ++db) acc[u][db] *= alpha;
@@ -320,9 +322,9 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
             if (r == KR) qr[u].h[0] = (__bf16)(m_ref[u] == -INFINITY ? 0.f : -m_ref[u]);
           }
         } else {  // d_r = 0 or 32: the shift rides in the accumulator start
-          const float shift = (mx == -INFINITY) ? 0.f : (unset || mx > kRescaleLog2P) ? mx : 0.f;
+          const float shift = (mx == -INFINITY) ? 0.f : (unset || mx > thr) ? mx : 0.f;
           if (__any(shift != 0.f)) {
-            const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-shift);  // unset: nothing accumulated
+            const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-shift * sl2);  // unset: nothing accumulated
             l_run[u] *= alpha;
 #pragma unroll
             for (int db = 0; db < 4; ++db) acc[u][db] *= alpha;
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_mfma_kernel(PrefillLa
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[st][i] = __builtin_amdgcn_exp2f(s[st][i]);
+        for (int i = 0; i < 4; ++i) s[st][i] = __builtin_amdgcn_exp2f(s[st][i] * sl2);
       float psum = s[0][0];  // (not 0 + ...: the compiler keeps an add of +0)
 #pragma unroll
       for (int e = 1; e < 16; ++e) psum += s[e >> 2][e & 3];

@@ -137,11 +137,16 @@ def test_rope_query_matches_oracle(dtype, d_r):
 # Decode
 # ---------------------------------------------------------------------------
 
-def _decode_post_rope(wl, lens, *, paged=False, split=0, seed=0):
+def _decode_post_rope(wl, lens, *, paged=False, split=0, seed=0, kr_boost=()):
     """Decode-only problem: k_r and q_rope drawn directly as rotated values.
-    Returns (gpu_out, oracle_out)."""
+    `kr_boost`: (first token, factor) pairs; the positional keys of every
+    sequence from that token on are multiplied by the factor (a power of two,
+    so the stored values stay exact). Returns (gpu_out, oracle_out)."""
     inp = W.make_gva_inputs(wl, lens=lens, seed=wl.seed + seed)
     kr_rot, q_rot = W.draw_post_rope(wl, inp.lens, seed=seed)
+    for t0, factor in kr_boost:
+        for rows in kr_rot:
+            rows[t0:] *= factor
     cap = max(int(max(lens)), 1)
     if paged:
         v, k, table, nblk = S.paged_cache_from_host(wl, inp.V, kr_rot, np.maximum(lens, 1), seed)
@@ -222,6 +227,20 @@ def test_split_and_paged_invariance():
             for p in (False, True) for s in (0, 64, 1024)]
     for o in outs[1:]:
         S.assert_close(o, outs[0], "bf16", "split/paged invariance")
+
+
+@pytest.mark.parametrize("paged,split", [(False, 0), (False, 64), (True, 256)])
+def test_decode_reference_moves_on_later_tiles(paged, split):
+    """Positional keys scaled by 8 from token 640 on and by 32 from token 1600
+    on: the later tiles' scores pass the first tiles' max by far more than 2^8
+    (log2 units), so every column's reference moves in the middle of the
+    sequence (the rescale branch of the online softmax), in some partitions
+    more than once."""
+    wl = _small_wl("bf16", 16, B=2)
+    lens = np.array([2100, 1700])
+    out, ref = _decode_post_rope(wl, lens, paged=paged, split=split, seed=41,
+                                 kr_boost=((640, 8.0), (1600, 4.0)))
+    S.assert_close(out, ref, "bf16", f"moving reference paged={paged} split={split}")
 
 
 @pytest.mark.parametrize("name", ["mid_bf16", "wide_dr24", "long_split", "ragged_paged"])

@@ -87,6 +87,51 @@ def test_prefill_matches_oracle(hpg, paged, nq):
         assert np.all(got[b, :max(nq - n, 0)] == 0)
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_prefill_reference_moves_on_later_tiles(paged):
+    """Positional keys scaled by 8 from token 200 on and by 32 from token 400
+    on (powers of two: the stored values stay exact): for the later queries
+    the scores of later tiles pass the first tile's max by far more than 2^8
+    (log2 units), so the columns' references move mid-sweep, in the rescale
+    branch of the online softmax. Keys and queries are drawn as rotated
+    values and handed to both sides as they are: with scores this large, a
+    one-unit difference in a rotated key's last place (which the rotation
+    is allowed) would move a weight by several percent. The values are
+    halved (exact) so that the outputs, which here follow single large-score
+    tokens, stay below 2.5: their own bf16 rounding then stays well inside
+    the absolute bound."""
+    wl = W.Workload("prefill_move", 9, B=2, H=16, G=4, d_n=64, d_v=64, d_r=16, S=0, dtype="bf16")
+    lens = np.array([700, 450])
+    nq = 700
+    inp = W.make_gva_inputs(wl, lens=lens, seed=110)
+    for rows in inp.V:
+        rows *= 0.5
+    kr_rot, _ = W.draw_post_rope(wl, lens, seed=110)
+    for rows in kr_rot:
+        rows[200:] *= 8.0
+        rows[400:] *= 4.0
+    qn, q_rot = _queries(wl, nq, seed=112)  # q_rot: drawn directly as rotated values
+    cap = int(max(lens))
+    print(f"[case] prefill moving reference paged={paged}", flush=True)
+    if paged:
+        v, k, table, nblk = S.paged_cache_from_host(wl, inp.V, kr_rot, lens, 113)
+        shape = gva.make_shape(wl.B, wl.H, wl.G, 64, 64, wl.d_r, max_seq_len=cap, block_size=64,
+                               num_blocks=nblk, max_blocks_per_seq=table.shape[1], dtype="bf16")
+    else:
+        v, k, _ = S.uniform_cache_from_host(wl, inp.V, kr_rot, cap, lens)
+        table = None
+        shape = gva.make_shape(wl.B, wl.H, wl.G, 64, 64, wl.d_r, capacity=cap, max_seq_len=cap, dtype="bf16")
+    seq = torch.tensor(lens.astype(np.int32), device="cuda")
+    out = torch.full((wl.B, nq, wl.H, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gva.gva_prefill(shape, nq, S.dev(qn, "bf16"), S.dev(q_rot, "bf16"), S.dev(inp.M, "bf16"), v, k, seq,
+                    table, wl.scale, out)
+    torch.cuda.synchronize()
+    got = S.host(out)
+    ref = O.gva_prefill(inp.V, kr_rot, qn, q_rot, inp.M, lens, wl.scale)
+    assert not np.isnan(got).any()
+    S.assert_close(got, ref, "bf16", f"prefill moving reference paged={paged}")
+
+
 @pytest.mark.parametrize("d_r", [0, 8, 24, 32])
 def test_prefill_positional_widths(d_r):
     wl = W.Workload("prefill_dr", 9, B=3, H=16, G=4, d_n=64, d_v=64, d_r=d_r, S=0, dtype="bf16")
