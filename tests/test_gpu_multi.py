@@ -86,6 +86,41 @@ def test_multi_matches_oracle(nq, hpg, paged, split):
         S.assert_close(got[:, j], ref[:, j], "bf16", f"multi nq={nq} hpg={hpg} query {j}")
 
 
+@pytest.mark.parametrize("nq", [2, 4])
+@pytest.mark.parametrize("split", [0, 256])
+def test_multi_reference_moves_on_later_tiles(nq, split):
+    """Positional keys scaled by 8 from token 640 on and by 32 from token 1600
+    on (exact powers of two), so the columns' softmax references move
+    mid-sequence; keys and queries drawn as rotated values and handed to both
+    sides as they are (a rotated key's last-place difference would otherwise
+    be amplified by these logits)."""
+    wl = W.Workload("multi_move", 9, B=2, H=16, G=4, d_n=64, d_v=64, d_r=16, S=0, dtype="bf16")
+    lens = np.array([2100, 1700])
+    inp = W.make_gva_inputs(wl, lens=lens, seed=90 + nq)
+    kr_rot, _ = W.draw_post_rope(wl, lens, seed=90 + nq)
+    for rows in kr_rot:
+        rows[640:] *= 8.0
+        rows[1600:] *= 4.0
+    rng = np.random.default_rng(91 + nq)
+    qn = W.round_storage(rng.standard_normal((wl.B, nq, wl.H, wl.d_n)), "bf16")
+    q_rot = W.round_storage(rng.standard_normal((wl.B, nq, wl.H, wl.d_r)), "bf16")
+    cap = int(max(lens))
+    v, k, seq = S.uniform_cache_from_host(wl, inp.V, kr_rot, cap, lens)
+    shape = gva.make_shape(wl.B, wl.H, wl.G, 64, 64, wl.d_r, capacity=cap, max_seq_len=cap,
+                           split_tokens=split, dtype="bf16")
+    out = torch.empty(wl.B, nq, wl.H, 64, dtype=torch.bfloat16, device="cuda")
+    nb = gva.gva_decode_multi_workspace_bytes(shape, nq)
+    ws = torch.zeros(max(nb, 4) // 4 + 1, dtype=torch.float32, device="cuda")
+    print(f"[case] multi moving reference nq={nq} split={split}", flush=True)
+    gva.gva_decode_multi(shape, nq, S.dev(qn, "bf16"), S.dev(q_rot, "bf16"), S.dev(inp.M, "bf16"), v, k, seq,
+                         None, wl.scale, out, ws)
+    torch.cuda.synchronize()
+    ref = O.gva_decode_multi(inp.V, kr_rot, qn, q_rot, inp.M, lens, wl.scale)
+    got = S.host(out)
+    for j in range(nq):
+        S.assert_close(got[:, j], ref[:, j], "bf16", f"multi moving reference nq={nq} split={split} query {j}")
+
+
 def test_multi_shorter_sequences_than_queries():
     """A sequence with fewer tokens than queries: the early queries read
     nothing and give zero rows; an empty sequence gives zeros throughout."""

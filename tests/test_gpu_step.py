@@ -24,9 +24,15 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _pair_of_caches(wl, lens, cap, paged, seed):
-    """Two identical caches (one per path) prefilled with the same tokens."""
+def _pair_of_caches(wl, lens, cap, paged, seed, kr_boost=()):
+    """Two identical caches (one per path) prefilled with the same tokens.
+    `kr_boost`: (first token, factor) pairs scaling the positional keys (before
+    rotation) of every sequence from that token on; powers of two keep them
+    exact."""
     inp = W.make_gva_inputs(wl, lens=lens, extra=8, seed=seed)
+    for t0, factor in kr_boost:
+        for rows in inp.kr:
+            rows[t0:] *= factor
     caches = []
     table = nblk = None
     if paged:
@@ -160,3 +166,33 @@ def test_step_from_empty_and_when_full():
             assert torch.equal(out_b[0], v1[0].repeat_interleave(4, dim=0))
     assert cb.seq_lens.cpu().tolist() == [4, 64]
     assert torch.equal(ca.v_cache, cb.v_cache) and torch.equal(ca.kr_cache, cb.kr_cache)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("split", [0, 256])
+def test_step_equals_three_calls_moving_reference(paged, split):
+    """Positional keys scaled by 8 from token 640 on and by 32 from token 1600
+    on, so the softmax reference of every column moves in the middle of the
+    sequence (the decode's rescale branch, checked against the oracle in the
+    parity tests): the fused step stays bit-identical to the three calls."""
+    wl = W.Workload("step_move", 9, B=3, H=16, G=4, d_n=64, d_v=64, d_r=16, S=0, dtype="bf16")
+    lens = np.array([2100, 1700, 900])
+    cap = 2200
+    inp, (ca, cb) = _pair_of_caches(wl, lens, cap, paged, seed=17, kr_boost=((640, 8.0), (1600, 4.0)))
+    qn, qr, Md = (S.dev(x, "bf16") for x in (inp.q_nope, inp.q_rope, inp.M))
+    out_a = torch.empty(wl.B, wl.H, 64, dtype=torch.bfloat16, device="cuda")
+    out_b = torch.empty_like(out_a)
+    q_rot = torch.empty_like(qr)
+    ws_b = cb.step_workspace(int(lens.max()) + 2, split)
+    for i in range(2):
+        max_len = int(lens.max()) + i + 1
+        print(f"[case] step moving reference paged={paged} split={split} i={i}", flush=True)
+        v1, k1 = _new_token(inp, lens, i, "bf16")
+        ca.append(v1.unsqueeze(2).contiguous(), k1.unsqueeze(1).contiguous(), BASE)
+        gva.gva_rope_query(ca.shape(max_len, split), qr, q_rot, ca.seq_lens, BASE)
+        ca.decode(qn, q_rot, Md, wl.scale, out_a, max_len, split)
+        cb.step(v1, k1, qn, qr, Md, wl.scale, out_b, max_len, split, workspace=ws_b)
+        torch.cuda.synchronize()
+        assert torch.equal(ca.seq_lens, cb.seq_lens)
+        assert torch.equal(out_a, out_b), (out_a.float() - out_b.float()).abs().max()
+        assert torch.isfinite(out_a.float()).all()
