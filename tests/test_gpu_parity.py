@@ -137,16 +137,22 @@ def test_rope_query_matches_oracle(dtype, d_r):
 # Decode
 # ---------------------------------------------------------------------------
 
-def _decode_post_rope(wl, lens, *, paged=False, split=0, seed=0, kr_boost=()):
+def _decode_post_rope(wl, lens, *, paged=False, split=0, seed=0, kr_boost=(), m_factor=1.0, v_factor=1.0):
     """Decode-only problem: k_r and q_rope drawn directly as rotated values.
     `kr_boost`: (first token, factor) pairs; the positional keys of every
-    sequence from that token on are multiplied by the factor (a power of two,
-    so the stored values stay exact). Returns (gpu_out, oracle_out)."""
+    sequence from that token on are multiplied by the factor. `m_factor`,
+    `v_factor` multiply the maps and the values. All factors are powers of
+    two, so the stored values stay exact. Returns (gpu_out, oracle_out)."""
     inp = W.make_gva_inputs(wl, lens=lens, seed=wl.seed + seed)
     kr_rot, q_rot = W.draw_post_rope(wl, inp.lens, seed=seed)
     for t0, factor in kr_boost:
         for rows in kr_rot:
             rows[t0:] *= factor
+    if m_factor != 1.0:
+        inp.M[...] *= m_factor
+    if v_factor != 1.0:
+        for rows in inp.V:
+            rows *= v_factor
     cap = max(int(max(lens)), 1)
     if paged:
         v, k, table, nblk = S.paged_cache_from_host(wl, inp.V, kr_rot, np.maximum(lens, 1), seed)
@@ -241,6 +247,19 @@ def test_decode_reference_moves_on_later_tiles(paged, split):
     out, ref = _decode_post_rope(wl, lens, paged=paged, split=split, seed=41,
                                  kr_boost=((640, 8.0), (1600, 4.0)))
     S.assert_close(out, ref, "bf16", f"moving reference paged={paged} split={split}")
+
+
+@pytest.mark.parametrize("paged,split", [(False, 0), (True, 256)])
+def test_decode_peaked_content_scores(paged, split):
+    """Maps scaled by 8 and values halved (exact): content logits with a
+    standard deviation of about 3.6 and the top ones well apart, far more
+    peaked than the N(0,1) workloads. The absorbed query q' = M q is the one
+    operand the kernel forms itself and rounds to bf16; the error this adds
+    grows with the logits and must stay inside the tolerance here."""
+    wl = _small_wl("bf16", 16, B=2)
+    lens = np.array([4097, 2500])
+    out, ref = _decode_post_rope(wl, lens, paged=paged, split=split, seed=51, m_factor=8.0, v_factor=0.5)
+    S.assert_close(out, ref, "bf16", f"peaked content scores paged={paged} split={split}")
 
 
 @pytest.mark.parametrize("name", ["mid_bf16", "wide_dr24", "long_split", "ragged_paged"])
