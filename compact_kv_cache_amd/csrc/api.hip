@@ -151,6 +151,10 @@ gva::DecodeLaunch make_decode(const gva_shape* s) {
   a.max_blocks = s->max_blocks_per_seq;
   a.split = resolve_split(s);
   a.n_split = n_splits(s, a.split);
+  // An explicit partition length whose partitions would fill two or more
+  // rounds of workgroups (>= 512 of them; one per compute unit) is served two
+  // partitions per workgroup: the same partials, in about half the rounds.
+  a.ppw = (s->split_tokens > 0 && a.n_split >= 2 && (int64_t)a.B * a.G * a.n_split >= 512) ? 2 : 1;
   a.paged = s->block_size != 0;
   a.bf16 = s->dtype == GVA_BF16;
   a.nq = 1;

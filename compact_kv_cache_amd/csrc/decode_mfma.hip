@@ -95,7 +95,7 @@ struct Frags {
 // kernel-argument fetch (a by-value struct is never preloaded). The launch
 // struct repeats them; the copies below take precedence. H and d_r follow
 // from the template (H = HPG * G, d_r = 8 * KR).
-template <int HPG, bool PAGED, int KR, bool GQA, bool STEP, int NQ>
+template <int HPG, bool PAGED, int KR, bool GQA, bool STEP, int NQ, bool PP2>
 __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void* arg_v_cache, const void* arg_kr_cache,
                                                                       const void* arg_M, const void* arg_q_nope,
                                                                       int arg_B, int arg_G, int arg_split,
@@ -123,6 +123,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
   static_assert(NQ == 1 || (!GQA && !STEP), "several queries: GVA decode only");
   static_assert(!(GQA && DR), "GQA reference has no positional slice");
   static_assert(!(GQA && STEP), "the fused step is GVA only");
+  // PP2: each workgroup takes two consecutive split-K partitions of its
+  // (sequence, group), the last one also an odd leftover (in practice the
+  // short tail of tokens appended past a multiple of the partition length),
+  // one after the other in one stream of tiles, and leaves a partial for
+  // each. Used where the partitions would otherwise need more than one round
+  // of workgroups: the second round's start-up and the first round's hand-off
+  // then overlap the stream instead of following it.
+  static_assert(!PP2 || (NQ == 1 && !GQA), "two partitions per workgroup: one query, GVA");
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
   const int col = lane & 15, r = lane >> 4;                 // MFMA column / lane group
@@ -143,18 +151,21 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
 
   // Workgroup id -> (sequence, partition) pair p and group g; the G groups of a
   // pair share id % 8 (one XCD) and have consecutive slots there.
-  const int pairs = a.B * a.n_split;
+  const int n_wsplit = PP2 ? max(a.n_split >> 1, 1) : a.n_split;  // workgroups per (sequence, group)
+  const int pairs = a.B * n_wsplit;
   const int q8 = blockIdx.x >> 3;
   const int g = q8 % G;
   const int p = (q8 / G) * 8 + (blockIdx.x & 7);
   if (p >= pairs) return;
-  const int b = p / a.n_split, split = p % a.n_split;
+  const int b = p / n_wsplit, ws = p % n_wsplit;
+  const int split = PP2 ? 2 * ws : ws;  // the workgroup's first partition
+  const int n_own = PP2 ? (ws == n_wsplit - 1 ? a.n_split - split : 2) : 1;  // its partitions: 1 to 3
 
   // Partition range from the host-side bound max_seq_len. It does not depend
   // on the stored lengths, so the first tiles are requested before seq_lens[b]
   // has arrived; rows past the stored length are cleared before any use.
   const int t_begin = split * a.split;
-  const int t_end_max = min(a.max_seq_len, t_begin + a.split);
+  const int t_end_max = min(a.max_seq_len, t_begin + n_own * a.split);
   const int tiles_max = max(t_end_max - t_begin + kTile - 1, 0) / kTile;
   const float sl2 = a.scale * kLog2e;
   const int ccol = col % NCOL;
@@ -311,15 +322,17 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
   // output: the only participant, or the last to arrive for the split-K
   // merge, which every other participant reaches first) and from every
   // workgroup whose partition lies past the stored length (after a barrier
-  // that follows its waves' reads). The last of these G * (1 + n_split -
-  // max(n_parts, 1)) arrivals stores the new length and clears the counter;
+  // that follows its waves' reads). The last of these G * (1 + workgroups per
+  // group - those holding tokens) arrivals stores the new length and clears
+  // the counter;
   // no workgroup of the call reads seq_lens[b] after it. The arrival is one
   // atomic per finalizer at the end, made by the first lane of the last wave,
   // which has no merge loads of its own (loads of a wave complete in order, so
   // an atomic ahead of them would delay them by its round trip).
   static_assert(!STEP || NCOL < kWaves, "the last wave is free during the merge");
   constexpr int kSeqThread = 64 * (kWaves - 1);
-  const int seq_arrivals = G * (1 + a.n_split - max(n_parts, 1));
+  const int n_wparts = PP2 ? min(n_wsplit, (max(n_parts, 1) + 1) >> 1) : max(n_parts, 1);  // holding tokens
+  const int seq_arrivals = G * (1 + n_wsplit - n_wparts);
   auto arrive_seq = [&]() {  // thread kSeqThread
     if constexpr (STEP) {
       const int ticket =
@@ -337,7 +350,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
     }
     return;
   }
-  const int t_end = min(n, t_begin + a.split);
+  const int t_end = min(n, t_begin + n_own * a.split);
   const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;  // 0 only when n == 0
   const int p_col = n - NQ + jq;       // last token this lane's query reads (several queries)
   const int causal_lo = n - NQ + 1;    // tokens before it are read by every query
@@ -600,8 +613,42 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
   // load on any path, so the reload is simply skipped after the wave's last
   // tile (an empty-range load would still take a slot in the request queue).
   Frags<DR> F;
+  // PP2: the softmax states of the workgroup's first and second partitions,
+  // set aside when the wave's tiles move on to the next partition (tiles
+  // kTPP and 2 kTPP onward of the range); `reached` counts them (uniform).
+  f32x4 acc_a[PP2 ? 4 : 1], acc_b[PP2 ? 4 : 1];
+  float m_a = -INFINITY, l_a = 0.f, m_b = -INFINITY, l_b = 0.f;
+  int reached = 0;
+  const int kTPP = a.split / kTile;
 #pragma clang loop unroll(disable)
   for (int k = w; k < n_tiles; k += kWaves) {
+    if constexpr (PP2) {
+      const int pk = (k >= kTPP) + (k >= 2 * kTPP);  // partition of this tile in the range
+      if (reached == 0 && pk >= 1) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          acc_a[db] = acc_o[db];
+          acc_o[db] = kZero4;
+        }
+        m_a = m_ref;
+        l_a = l_run;
+        m_ref = -INFINITY;
+        l_run = 0.f;
+        reached = 1;
+      }
+      if (reached == 1 && pk >= 2) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          acc_b[db] = acc_o[db];
+          acc_o[db] = kZero4;
+        }
+        m_b = m_ref;
+        l_b = l_run;
+        m_ref = -INFINITY;
+        l_run = 0.f;
+        reached = 2;
+      }
+    }
     stage(X);
     fragments(F, X);
     if (k + kWaves < n_tiles) issue(X, k + kWaves, t_end, n_tiles);  // wave-uniform
@@ -609,18 +656,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
   }
 
   // ---- merge the waves ----------------------------------------------------------------
-  l_run = rows_sum(l_run);
-  if (col < NCOL) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red_o[w][col][16 * db + 4 * r + i] = acc_o[db][i];
-    if (r == 0) {
-      red_ml[w][col][0] = m_ref * sl2;  // log2 units (-inf for a wave without tiles)
-      red_ml[w][col][1] = l_run;
-    }
-  }
-  __syncthreads();
   // merge thread: column jj = wave + 8u (query jj / HPG, head jj % HPG), channel d
   constexpr int kPer = (NCOL + kWaves - 1) / kWaves;
   const int d = lane;
@@ -629,23 +664,74 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int jj = (tid >> 6) + u * kWaves;
-    o[u] = 0.f;
-    l[u] = 0.f;
-    mfin[u] = -INFINITY;
     orow[u] = ((int64_t)b * NQ + jj / HPG) * H + g * HPG + jj % HPG;
-    if (jj < NCOL) {
+  }
+  // One partition's state of the eight waves, merged in LDS into o, l, mfin.
+  auto merge_waves = [&](const f32x4 (&acc)[4], float m_w, float l_w) {
+    l_w = rows_sum(l_w);
+    if (col < NCOL) {
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) mfin[u] = fmaxf(mfin[u], red_ml[ww][jj][0]);
-      if (mfin[u] > -INFINITY) {
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-          const float f = exp2f(red_ml[ww][jj][0] - mfin[u]);
-          o[u] = fmaf(f, red_o[ww][jj][d], o[u]);
-          l[u] = fmaf(f, red_ml[ww][jj][1], l[u]);
+        for (int i = 0; i < 4; ++i) red_o[w][col][16 * db + 4 * r + i] = acc[db][i];
+      if (r == 0) {
+        red_ml[w][col][0] = m_w * sl2;  // log2 units (-inf for a wave without tiles)
+        red_ml[w][col][1] = l_w;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int jj = (tid >> 6) + u * kWaves;
+      o[u] = 0.f;
+      l[u] = 0.f;
+      mfin[u] = -INFINITY;
+      if (jj < NCOL) {
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) mfin[u] = fmaxf(mfin[u], red_ml[ww][jj][0]);
+        if (mfin[u] > -INFINITY) {
+#pragma unroll
+          for (int ww = 0; ww < kWaves; ++ww) {
+            const float f = exp2f(red_ml[ww][jj][0] - mfin[u]);
+            o[u] = fmaf(f, red_o[ww][jj][d], o[u]);
+            l[u] = fmaf(f, red_ml[ww][jj][1], l[u]);
+          }
         }
       }
     }
-  }
+  };
+  auto store_partial = [&](int part) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      if ((tid >> 6) + u * kWaves < NCOL) {
+        const int64_t slot = orow[u] * a.n_split + part;
+        st_dev(a.ws_o + slot * kD + d, o[u]);
+        if (d == 0) {
+          st_dev(a.ws_ml + 2 * slot, mfin[u]);
+          st_dev(a.ws_ml + 2 * slot + 1, l[u]);
+        }
+      }
+    }
+  };
+  // Partition j of the range: set aside if the wave went past it, live if it
+  // is the wave's current one, empty if the wave has no tile there. (Selected
+  // per wave, then merged by every wave together: the merge holds a
+  // workgroup barrier.)
+  auto merge_part = [&](int j) {
+    if constexpr (PP2) {
+      const bool aside = reached > j, live = reached == j;
+      f32x4 acc_j[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        acc_j[db] = aside ? (j == 0 ? acc_a[db] : acc_b[db]) : (live ? acc_o[db] : kZero4);
+      const float m_j = aside ? (j == 0 ? m_a : m_b) : (live ? m_ref : -INFINITY);
+      const float l_j = aside ? (j == 0 ? l_a : l_b) : (live ? l_run : 0.f);
+      merge_waves(acc_j, m_j, l_j);
+    } else {
+      merge_waves(acc_o, m_ref, l_run);
+    }
+  };
+  merge_part(0);
   __bf16* out = reinterpret_cast<__bf16*>(a.out);
   if (n_parts <= 1) {
     if (tid == kSeqThread) arrive_seq();
@@ -654,19 +740,18 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
       if ((tid >> 6) + u * kWaves < NCOL) out[orow[u] * kD + d] = (__bf16)(l[u] > 0.f ? o[u] / l[u] : 0.f);
     return;
   }
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    if ((tid >> 6) + u * kWaves < NCOL) {
-      const int64_t slot = orow[u] * a.n_split + split;
-      st_dev(a.ws_o + slot * kD + d, o[u]);
-      if (d == 0) {
-        st_dev(a.ws_ml + 2 * slot, mfin[u]);
-        st_dev(a.ws_ml + 2 * slot + 1, l[u]);
-      }
+  store_partial(split);
+  // partitions of the range that hold tokens (uniform)
+  const int arrivals = min(split + n_own, n_parts) - split;
+  if constexpr (PP2) {
+    for (int j = 1; j < arrivals; ++j) {
+      __syncthreads();  // every thread is done reading the previous partition's state
+      merge_part(j);
+      store_partial(split + j);
     }
   }
   int32_t* counter = a.counters + ((int64_t)b * G + g) * kCounterStride;
-  if (arrive_last(counter, n_parts)) {
+  if (arrive_last(counter, n_parts, arrivals)) {
     if (tid == kSeqThread) arrive_seq();
 #pragma unroll
     for (int u = 0; u < kPer; ++u)
@@ -676,17 +761,25 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
   }
 }
 
-template <int HPG, int KR, bool GQA, bool STEP, int NQ>
-hipError_t mfma_launch(const DecodeLaunch& a, hipStream_t s) {
-  const int pairs = a.B * a.n_split;
+template <int HPG, int KR, bool GQA, bool STEP, int NQ, bool PP2>
+hipError_t mfma_launch_ppw(const DecodeLaunch& a, hipStream_t s) {
+  const int pairs = a.B * (PP2 ? max(a.n_split >> 1, 1) : a.n_split);
   const dim3 grid(((pairs + 7) / 8) * 8 * a.G);
   if (a.paged)
-    decode_mfma_kernel<HPG, true, KR, GQA, STEP, NQ><<<grid, 64 * kWaves, 0, s>>>(
+    decode_mfma_kernel<HPG, true, KR, GQA, STEP, NQ, PP2><<<grid, 64 * kWaves, 0, s>>>(
         a.v_cache, a.kr_cache, a.M, a.q_nope, a.B, a.G, a.split, a.n_split, a.max_seq_len, a.capacity, a);
   else
-    decode_mfma_kernel<HPG, false, KR, GQA, STEP, NQ><<<grid, 64 * kWaves, 0, s>>>(
+    decode_mfma_kernel<HPG, false, KR, GQA, STEP, NQ, PP2><<<grid, 64 * kWaves, 0, s>>>(
         a.v_cache, a.kr_cache, a.M, a.q_nope, a.B, a.G, a.split, a.n_split, a.max_seq_len, a.capacity, a);
   return hipGetLastError();
+}
+
+template <int HPG, int KR, bool GQA, bool STEP, int NQ>
+hipError_t mfma_launch(const DecodeLaunch& a, hipStream_t s) {
+  if constexpr (NQ == 1 && !GQA) {
+    if (a.ppw == 2) return mfma_launch_ppw<HPG, KR, GQA, STEP, NQ, true>(a, s);
+  }
+  return mfma_launch_ppw<HPG, KR, GQA, STEP, NQ, false>(a, s);
 }
 
 // queries per sequence: 1 (every path), 2 or 4 (GVA decode of several new tokens)

@@ -182,16 +182,17 @@ __device__ __forceinline__ float ld_dev(const float* p) {
 }
 
 // Must be reached by every thread of the workgroup; returns the same value in
-// all of them.
-__device__ __forceinline__ bool arrive_last(int32_t* counter, int n_parts) {
+// all of them. `arrivals`: partials this workgroup contributes (its count on
+// the counter).
+__device__ __forceinline__ bool arrive_last(int32_t* counter, int n_parts, int arrivals = 1) {
   __shared__ int s_last;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();                // ... and so are every other wave's
   if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (old == n_parts - 1);
+    const int old = __hip_atomic_fetch_add(counter, arrivals, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old + arrivals == n_parts);
   }
   __syncthreads();
   return s_last != 0;
@@ -203,11 +204,13 @@ __device__ __forceinline__ void reset_counter(int32_t* counter) {
 
 // Log-sum-exp merge of n_parts partials of one head for channel d:
 // out = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s, M = max_s m_s, with
-// m_s in log2 units and o_s unnormalized. Partials are fetched eight at a
-// time with all loads in flight together, merged online across batches.
-__device__ __forceinline__ float merge_partials(const float* o, const float* ml, int64_t slot0,
-                                                int n_parts, int d) {
-  constexpr int K = 8;
+// m_s in log2 units and o_s unnormalized. Partials are fetched K at a time
+// with all loads in flight together, merged online across batches: K = 8 for
+// up to 8 partials, else 16 (48 loads, within the 63 a wave can count), so a
+// long split pays fewer round trips.
+template <int K>
+__device__ __forceinline__ float merge_partials_k(const float* o, const float* ml, int64_t slot0,
+                                                  int n_parts, int d) {
   float M = -INFINITY, num = 0.f, den = 0.f;
   for (int base = 0; base < n_parts; base += K) {
     float mv[K], lv[K], ov[K];
@@ -236,6 +239,11 @@ __device__ __forceinline__ float merge_partials(const float* o, const float* ml,
     M = bm;
   }
   return den > 0.f ? num / den : 0.f;
+}
+
+__device__ __forceinline__ float merge_partials(const float* o, const float* ml, int64_t slot0,
+                                                int n_parts, int d) {
+  return n_parts <= 8 ? merge_partials_k<8>(o, ml, slot0, n_parts, d) : merge_partials_k<16>(o, ml, slot0, n_parts, d);
 }
 
 }  // namespace gva

@@ -66,6 +66,7 @@ struct DecodeLaunch {
   int B, H, G, d_r, capacity, max_seq_len, num_blocks, max_blocks;
   int split, n_split;  // split-K partition length and count
   int nq;              // queries per sequence (the last nq tokens; 1, 2 or 4)
+  int ppw;             // split-K partitions per workgroup: 1 or 2 (one query, GVA kernels)
   bool paged, bf16;
   const void* q_nope;  // GQA: q
   const void* q_rope;  // rotated; fused step: before RoPE

@@ -85,6 +85,10 @@ typedef enum gva_dtype {
  *                    512 tokens, sized so that the B*G*partitions workgroups
  *                    fill the 256 compute units in one round; when B*G >= 256
  *                    and the longest sequence has >= 480 tiles, thirds of it.
+ *                    An explicit length whose B*G*partitions reach 512 or more
+ *                    is served two partitions per workgroup (the last one of
+ *                    a sequence and group takes an odd leftover too); every
+ *                    partition still leaves its own partial for the merge.
  *   dtype            storage dtype of q, M, caches and out
  *
  * Cache layouts (call dtype):

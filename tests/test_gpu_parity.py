@@ -262,6 +262,23 @@ def test_decode_peaked_content_scores(paged, split):
     S.assert_close(out, ref, "bf16", f"peaked content scores paged={paged} split={split}")
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_decode_two_partitions_per_workgroup(paged):
+    """An explicit 64-token partition length over 33 partitions and 16
+    (sequence, group) pairs (528 partitions, more than two rounds of
+    workgroups) is served two partitions per workgroup. Lengths: an odd and
+    an even partition count in the last workgroup, a sequence that ends
+    halfway (workgroups past it exit early) and an empty one; against the
+    oracle, and against a partition length that keeps one per workgroup."""
+    wl = _small_wl("bf16", 16, B=4)
+    lens = np.array([2100, 2112, 1000, 0])
+    out, ref = _decode_post_rope(wl, lens, paged=paged, split=64, seed=61)
+    S.assert_close(out, ref, "bf16", f"two partitions per workgroup paged={paged}")
+    assert np.array_equal(out[3], np.zeros_like(out[3]))
+    out1, _ = _decode_post_rope(wl, lens, paged=paged, split=128, seed=61)
+    S.assert_close(out, out1, "bf16", "two partitions per workgroup against one")
+
+
 @pytest.mark.parametrize("name", ["mid_bf16", "wide_dr24", "long_split", "ragged_paged"])
 def test_decode_full_size(name):
     wl = W.WORKLOADS[name]

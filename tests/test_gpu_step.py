@@ -196,3 +196,37 @@ def test_step_equals_three_calls_moving_reference(paged, split):
         assert torch.equal(ca.seq_lens, cb.seq_lens)
         assert torch.equal(out_a, out_b), (out_a.float() - out_b.float()).abs().max()
         assert torch.isfinite(out_a.float()).all()
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_step_two_partitions_per_workgroup(paged):
+    """64-token partitions over 33-34 partitions and 16 (sequence, group)
+    pairs: two partitions per workgroup in the fused step and in the decode
+    of the three calls, bit for bit equal, and the step against the oracle's
+    step; the steps carry the longest sequence across a partition boundary."""
+    wl = W.Workload("step_ppw", 9, B=4, H=16, G=4, d_n=64, d_v=64, d_r=16, S=0, dtype="bf16")
+    lens = np.array([2111, 2048, 1000, 0])
+    cap = 2200
+    split = 64
+    inp, (ca, cb) = _pair_of_caches(wl, lens, cap, paged, seed=27)
+    qn, qr, Md = (S.dev(x, "bf16") for x in (inp.q_nope, inp.q_rope, inp.M))
+    out_a = torch.empty(wl.B, wl.H, 64, dtype=torch.bfloat16, device="cuda")
+    out_b = torch.empty_like(out_a)
+    q_rot = torch.empty_like(qr)
+    ws_b = cb.step_workspace(int(lens.max()) + 2, split)
+    for i in range(2):
+        max_len = int(lens.max()) + i + 1
+        print(f"[case] step two partitions per workgroup paged={paged} i={i}", flush=True)
+        v1, k1 = _new_token(inp, lens, i, "bf16")
+        ca.append(v1.unsqueeze(2).contiguous(), k1.unsqueeze(1).contiguous(), BASE)
+        gva.gva_rope_query(ca.shape(max_len, split), qr, q_rot, ca.seq_lens, BASE)
+        ca.decode(qn, q_rot, Md, wl.scale, out_a, max_len, split)
+        cb.step(v1, k1, qn, qr, Md, wl.scale, out_b, max_len, split, workspace=ws_b)
+        torch.cuda.synchronize()
+        assert torch.equal(ca.seq_lens, cb.seq_lens)
+        assert torch.equal(out_a, out_b), (out_a.float() - out_b.float()).abs().max()
+        ref = O.gva_decode_step(inp.V, inp.kr, inp.q_nope, inp.q_rope, inp.M, lens + i + 1, wl.scale, BASE,
+                                "bf16")
+        S.assert_close(S.host(out_b), ref, "bf16", f"step two partitions per workgroup i={i}")
+    assert torch.equal(ca.v_cache, cb.v_cache)
+    assert torch.equal(ca.kr_cache, cb.kr_cache)
