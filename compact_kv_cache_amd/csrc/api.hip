@@ -115,6 +115,9 @@ size_t workspace_for(const gva_shape* s, int nq = 1) {
   return gva::ws_total_bytes(s->B, s->H, s->G, n_splits(s, split), nq);
 }
 
+// The partials' (m, l) pairs are read and written as 8-byte words.
+bool misaligned(const void* workspace) { return (reinterpret_cast<uintptr_t>(workspace) & 15) != 0; }
+
 void set_workspace(gva::DecodeLaunch& a, void* workspace) {
   if (!workspace) return;
   char* base = static_cast<char*>(workspace);
@@ -266,6 +269,7 @@ gva_status gva_decode_multi(const gva_shape* shape, int32_t n_q, const void* q_n
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && misaligned(workspace)) return fail(GVA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   gva::DecodeLaunch a = make_decode(shape);
   a.nq = n_q;
   a.q_nope = q_nope;
@@ -348,6 +352,7 @@ gva_status gva_decode_step(const gva_shape* shape, const void* v_new, const void
   if (!workspace || workspace_bytes < need)
     return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
+  if (misaligned(workspace)) return fail(GVA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   const bool paged = shape->block_size != 0;
   const int cap_tokens = paged ? shape->max_blocks_per_seq * 64 : shape->capacity;
   if (shape->dtype == GVA_BF16 && !force_valu()) {
@@ -535,6 +540,7 @@ gva_status gva_gqa_ref_decode(const gva_shape* shape, const void* q, const void*
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GVA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && misaligned(workspace)) return fail(GVA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   gva::DecodeLaunch a = make_decode(shape);
   a.q_nope = q;
   a.v_cache = v_cache;

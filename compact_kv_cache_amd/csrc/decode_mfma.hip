@@ -687,15 +687,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
       l[u] = 0.f;
       mfin[u] = -INFINITY;
       if (jj < NCOL) {
+        // every LDS read of the merge in flight at once, then the arithmetic
+        float2 ml8[kWaves];
+        float ov[kWaves];
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) mfin[u] = fmaxf(mfin[u], red_ml[ww][jj][0]);
-        if (mfin[u] > -INFINITY) {
+        for (int ww = 0; ww < kWaves; ++ww) {
+          ml8[ww] = *reinterpret_cast<const float2*>(&red_ml[ww][jj][0]);
+          ov[ww] = red_o[ww][jj][d];
+        }
 #pragma unroll
-          for (int ww = 0; ww < kWaves; ++ww) {
-            const float f = exp2f(red_ml[ww][jj][0] - mfin[u]);
-            o[u] = fmaf(f, red_o[ww][jj][d], o[u]);
-            l[u] = fmaf(f, red_ml[ww][jj][1], l[u]);
-          }
+        for (int ww = 0; ww < kWaves; ++ww) mfin[u] = fmaxf(mfin[u], ml8[ww].x);
+        const float mref = mfin[u] == -INFINITY ? 0.f : mfin[u];  // no wave holds tokens: weights 0
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float f = __builtin_amdgcn_exp2f(ml8[ww].x - mref);
+          o[u] = fmaf(f, ov[ww], o[u]);
+          l[u] = fmaf(f, ml8[ww].y, l[u]);
         }
       }
     }
@@ -706,10 +713,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
       if ((tid >> 6) + u * kWaves < NCOL) {
         const int64_t slot = orow[u] * a.n_split + part;
         st_dev(a.ws_o + slot * kD + d, o[u]);
-        if (d == 0) {
-          st_dev(a.ws_ml + 2 * slot, mfin[u]);
-          st_dev(a.ws_ml + 2 * slot + 1, l[u]);
-        }
+        if (d == 0) st_dev_ml(a.ws_ml + 2 * slot, mfin[u], l[u]);
       }
     }
   };

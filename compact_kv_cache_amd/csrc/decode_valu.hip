@@ -114,8 +114,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeLaunch a) {
   if (w < HPG) {
     st_dev(a.ws_o + (slot0 + split) * kD + lane, o);
     if (lane == 0) {
-      st_dev(a.ws_ml + 2 * (slot0 + split), m);
-      st_dev(a.ws_ml + 2 * (slot0 + split) + 1, l);
+      st_dev_ml(a.ws_ml + 2 * (slot0 + split), m, l);
     }
   }
   int32_t* counter = a.counters + ((int64_t)b * a.G + g) * kCounterStride;

@@ -180,6 +180,16 @@ __device__ __forceinline__ void st_dev(float* p, float v) {
 __device__ __forceinline__ float ld_dev(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A partial's (m, l) pair (adjacent floats, 8-byte aligned) as one 8-byte
+// device-coherent store or load: one memory instruction instead of two.
+__device__ __forceinline__ void st_dev_ml(float* p, float m, float l) {
+  const uint64_t v = (uint64_t)__float_as_uint(m) | ((uint64_t)__float_as_uint(l) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev_ml(const float* p) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Must be reached by every thread of the workgroup; returns the same value in
 // all of them. `arrivals`: partials this workgroup contributes (its count on
@@ -205,9 +215,9 @@ __device__ __forceinline__ void reset_counter(int32_t* counter) {
 // Log-sum-exp merge of n_parts partials of one head for channel d:
 // out = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s, M = max_s m_s, with
 // m_s in log2 units and o_s unnormalized. Partials are fetched K at a time
-// with all loads in flight together, merged online across batches: K = 8 for
-// up to 8 partials, else 16 (48 loads, within the 63 a wave can count), so a
-// long split pays fewer round trips.
+// with all loads in flight together, merged online across batches of K = 16
+// (48 loads, within the 63 a wave can count), so a long split pays fewer
+// round trips; up to 8 partials take one exact batch (merge_partials_n).
 template <int K>
 __device__ __forceinline__ float merge_partials_k(const float* o, const float* ml, int64_t slot0,
                                                   int n_parts, int d) {
@@ -241,9 +251,48 @@ __device__ __forceinline__ float merge_partials_k(const float* o, const float* m
   return den > 0.f ? num / den : 0.f;
 }
 
+// The same merge for exactly N partials, one batch: N loads of o and N of the
+// (m, l) pairs. Every vector memory instruction occupies the compute unit's
+// address unit for the same time whatever its width, so the merge that ends
+// the split-K hand-off issues only the loads it needs. Same arithmetic and
+// order as merge_partials_k, bit for bit.
+template <int N>
+__device__ __forceinline__ float merge_partials_n(const float* o, const float* ml, int64_t slot0, int d) {
+  float mv[N], lv[N], ov[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint64_t e = ld_dev_ml(ml + 2 * (slot0 + i));
+    mv[i] = __uint_as_float((uint32_t)e);
+    lv[i] = __uint_as_float((uint32_t)(e >> 32));
+    ov[i] = ld_dev(o + (slot0 + i) * kD + d);
+  }
+  float bm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < N; ++i) bm = fmaxf(bm, mv[i]);
+  const float rescale = exp2f(-INFINITY - bm);  // 0, or NaN when every partial is empty
+  float num = 0.f * rescale, den = 0.f * rescale;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float w = exp2f(mv[i] - bm);
+    num = fmaf(w, ov[i], num);
+    den = fmaf(w, lv[i], den);
+  }
+  return den > 0.f ? num / den : 0.f;
+}
+
 __device__ __forceinline__ float merge_partials(const float* o, const float* ml, int64_t slot0,
                                                 int n_parts, int d) {
-  return n_parts <= 8 ? merge_partials_k<8>(o, ml, slot0, n_parts, d) : merge_partials_k<16>(o, ml, slot0, n_parts, d);
+  switch (n_parts) {
+    case 1: return merge_partials_n<1>(o, ml, slot0, d);
+    case 2: return merge_partials_n<2>(o, ml, slot0, d);
+    case 3: return merge_partials_n<3>(o, ml, slot0, d);
+    case 4: return merge_partials_n<4>(o, ml, slot0, d);
+    case 5: return merge_partials_n<5>(o, ml, slot0, d);
+    case 6: return merge_partials_n<6>(o, ml, slot0, d);
+    case 7: return merge_partials_n<7>(o, ml, slot0, d);
+    case 8: return merge_partials_n<8>(o, ml, slot0, d);
+    default: return merge_partials_k<16>(o, ml, slot0, n_parts, d);
+  }
 }
 
 }  // namespace gva

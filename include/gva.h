@@ -178,7 +178,8 @@ gva_status gva_rope_query_multi(const gva_shape* shape, int32_t n_q, const void*
  *   out      [B][H][d_v]      call dtype; rows with seq_lens[b] <= 0 are zero
  *   workspace, workspace_bytes   device scratch of at least
  *            gva_decode_workspace_bytes(shape) bytes (may be NULL/0 when that
- *            is 0). It must be zero-filled before its first use; every call
+ *            is 0), 16-byte aligned (GVA_ERR_WORKSPACE otherwise; device
+ *            allocations are). It must be zero-filled before its first use; every call
  *            that completes leaves it ready for the next one (its arrival
  *            counters return to zero). Calls that overlap in time need
  *            distinct workspaces.

@@ -139,6 +139,7 @@ def test_decode_rejects_missing_pointers_and_workspace():
     assert _decode_status(s, FAKE, 1 << 30, kr=None) == _lib.GVA_ERR_INVALID_ARGUMENT
     assert _decode_status(s, None, 0) == _lib.GVA_ERR_WORKSPACE
     assert _decode_status(s, FAKE, 256 + 540671) == _lib.GVA_ERR_WORKSPACE
+    assert _decode_status(s, FAKE + 8, 1 << 30) == _lib.GVA_ERR_WORKSPACE   # (m, l) pairs: 8-byte words
     paged = _shape(block_size=64, num_blocks=100, max_blocks_per_seq=2048, capacity=0)
     assert _decode_status(paged, FAKE, 1 << 30, table=None) == _lib.GVA_ERR_INVALID_ARGUMENT
     assert gva.lib.gva_decode(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1.0, FAKE, None, 0,
