@@ -12,12 +12,15 @@ reads data that has not been touched for more than the 256 MB last-level
 cache; the default workload is B=16, S=4096, H=16, G=4, d_v=d_n=64, d_r=16,
 bf16 (the mid workload), on seeded synthetic data.
 
-Prints one JSON line. `value` = steps/s of the whole path (graph-replayed, so
-host launch overhead is excluded). `roofline` describes the one kernel of the
-timed region (the fused step): algorithmic cache bytes per step over its
-average launch duration, from HIP events around the graph replay on the
-stream the kernels run on. gva_decode alone (one kernel, no append) is timed
-the same way and reported beside it.
+Prints one JSON line. `value` = steps/s of the whole path: K steps launched
+back to back on one stream, queued behind a spin kernel that outlasts the
+host's launch loop, so the HIP events around them measure the device running
+the K steps, not the host launching them (a graph replay of the same steps is
+reported beside it; it adds a fixed start cost of its own per replay).
+`roofline` describes the one kernel of the timed region (the fused step):
+algorithmic cache bytes per step over its average launch duration, from the
+events on the stream the kernels run on. gva_decode alone (one kernel, no
+append) is timed the same way and reported beside it.
 
 `--mode gqa` instead times gva_decode against the same-shape GQA reference
 (gva_gqa_ref_decode, K and V caches) on the wide workload and reports the
@@ -47,11 +50,49 @@ METRIC = "GVA decode steps/s + effective cache-read GB/s (% HBM peak), B=16 S=40
 
 def hold_device():
     """Keep the GPU busy for about a millisecond (a spin kernel on the current
-    stream) while the host enqueues the timed region, so that the events
-    bracket the K steps as the device runs them back to back, not the host's
-    submission of the graph before its first kernel."""
+    stream) while the host enqueues a graph replay, so that the events bracket
+    the replay as the device runs it, not the host's submission of the graph
+    before its first kernel."""
     import torch
     torch.cuda._sleep(2_000_000)
+
+
+def queued_time(launch, n_warm: int, K: int, host_us: float, before_timed=None):
+    """Device time per call (ms) of K calls of `launch()` run back to back on
+    the current stream, HIP events around them on that stream.
+
+    The calls are enqueued behind a spin kernel that outlasts the host's
+    enqueueing, after `n_warm` untimed calls queued right before them, so the
+    events bracket the device's back-to-back execution of exactly K calls and
+    not the host's launch loop. If the device reached the first timed call
+    before the host had enqueued the last one (the start event completed
+    early), the spin is lengthened from the measured host rate and the
+    measurement repeated; host gaps could only have made the time longer.
+    The spin is sized from `host_us`, the host's time per launch call, with a
+    30% margin: a much longer one lets the clocks drop while one wave spins,
+    and the first timed steps then run slower (measured: 10.8-10.9 us per
+    mid step after a 0.5-1 ms spin, 11.0-11.1 us after 2-4 ms).
+    Returns (ms per call, attempts)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for attempt in range(1, 4):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int((n_warm + K) * host_us * 2.4e3 * 1.3) + 300_000)  # GPU clock cycles
+        t0 = time.perf_counter()
+        for _ in range(n_warm):
+            launch()
+        if before_timed is not None:
+            before_timed()
+        e0.record()
+        for _ in range(K):
+            launch()
+        e1.record()
+        ahead = not e0.query()
+        host_us = max(host_us, 1.5 * (time.perf_counter() - t0) * 1e6 / (n_warm + K))
+        torch.cuda.synchronize()
+        if ahead:
+            return e0.elapsed_time(e1) / K, attempt
+    raise RuntimeError("the host could not stay ahead of the device: timing would include launch gaps")
 
 
 def parse():
@@ -129,7 +170,7 @@ def main():
     cache_bytes = wl.B * wl.S * bpt
     R = args.replicas or max(2, math.ceil(512e6 / cache_bytes))
     K, Wm = args.steps, args.warmup
-    total_steps = Wm + 4 * K + 8
+    total_steps = 3 * Wm + 8 * K + 8  # (queued regions may be repeated, see queued_time)
     per_rep = math.ceil(total_steps / R) + 1
     cap = wl.S + per_rep
 
@@ -220,32 +261,40 @@ def main():
         return
 
     # Warm-up: the W untimed steps. The first two run eagerly, one of each
-    # form of the step (loading both paths); with a graph, the rest run as a
-    # graph of fused steps replayed right before the timed replay, so the
-    # timed steps start on a busy device in steady state.
+    # form of the step (loading both paths), then synchronized; the rest are
+    # queued right before the timed steps, so those start on a busy device in
+    # steady state.
     use_graph = not args.no_graph
-    i_step = 0
-    n_eager = Wm if not use_graph else min(Wm, 2)
-    for k in range(n_eager):
-        (fused_step if k % 2 == 0 else step)(i_step)
-        i_step += 1
-    torch.cuda.synchronize()
+    n_eager = min(Wm, 2)
+    counter = [0]
 
-    def graph_time(fn, first, warm=0):
-        """Capture `warm` calls of fn into one graph and the next K into
-        another; replay the first (untimed) and, right behind it on the
-        device, the second between events."""
+    def next_index():
+        counter[0] += 1
+        return counter[0] - 1
+
+    for k in range(n_eager):
+        (fused_step if k % 2 == 0 else step)(next_index())
+    torch.cuda.synchronize()
+    # host time per launch call through the Python binding (the first calls
+    # above include one-time loading, so not measured there); queued_time
+    # lengthens the spin from the measured rate if the host falls behind
+    host_us_fused, host_us_three = 25.0, 75.0
+
+    def graph_time(fn, warm=0):
+        """The same K steps captured in one graph (after `warm` untimed steps
+        in a graph of their own) and replayed behind the spin kernel: the
+        replay's fixed start cost (about 13 us) lands inside the events."""
         gw = None
         if warm > 0:
             gw = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gw):
                 for k in range(warm):
-                    fn(first + k)
-        step_bytes.clear()  # the timed steps' bytes only
+                    fn(next_index())
+        step_bytes.clear()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for k in range(K):
-                fn(first + warm + k)
+                fn(next_index())
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         hold_device()
@@ -257,33 +306,24 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / K
 
-    # ---- timed region 1: the whole step, one launch (gva_decode_step) --------
-    step_bytes.clear()
-    if use_graph:
-        n_graph_warm = Wm - n_eager
-        ms_step = graph_time(fused_step, i_step, n_graph_warm)
-        i_step += n_graph_warm
-    else:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for k in range(K):
-            fused_step(i_step + k)
-        torch.cuda.synchronize()
-        ms_step = (time.perf_counter() - t0) * 1e3 / K
-    i_step += K
+    # ---- timed region 1: the whole step, one launch (gva_decode_step), K
+    # launches back to back behind the spin kernel --------------------------
+    n_queued_warm = Wm - n_eager
+    ms_step, step_attempts = queued_time(lambda: fused_step(next_index()), n_queued_warm, K, host_us_fused,
+                                         before_timed=step_bytes.clear)
     mean_step_bytes = float(np.mean(step_bytes))
+    ms_per_step = ms_step
     # the same step as three calls (append, rope_query, decode)
-    ms_three = graph_time(step, i_step) if use_graph else None
-    i_step += K if use_graph else 0
-    # eager (host-launched) fused steps
+    ms_three, _ = queued_time(lambda: step(next_index()), 0, K, host_us_three)
+    # the fused step replayed from a graph (the former timing method)
+    ms_graph = graph_time(fused_step, n_queued_warm) if use_graph else None
+    # eager (host-launched) fused steps, host clock: the Python launch rate
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
-        fused_step(i_step + k)
+        fused_step(next_index())
     torch.cuda.synchronize()
     ms_eager = (time.perf_counter() - t0) * 1e3 / K
-    i_step += K
-    ms_per_step = ms_step
 
     # ---- timed region 2: decode kernel alone, HIP events around each call --
     stream = torch.cuda.current_stream()
@@ -302,25 +342,18 @@ def main():
     dec_ms_mean = float(np.mean(dec_ms))
     dec_bytes_mean = float(np.mean(dec_bytes))
 
-    # ---- timed region 3: K decode launches back to back (one graph), HIP
-    # events around the whole run on the launch stream: the average launch
-    # duration without per-call event overhead (this is the figure the
+    # ---- timed region 3: K decode launches back to back behind the spin
+    # kernel, HIP events around the whole run on the launch stream: the
+    # average launch duration without per-call event overhead (the figure the
     # kernel trace's average reproduces)
-    ms_dec_graph = None
-    if use_graph:
-        g2 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g2):
-            for k in range(K):
-                decode(k % R)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        hold_device()
-        e0.record()
-        g2.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms_dec_graph = e0.elapsed_time(e1) / K
-    ms_launch = ms_dec_graph if ms_dec_graph is not None else dec_ms_mean
+    dec_i = [0]
+
+    def next_decode():
+        decode(dec_i[0] % R)
+        dec_i[0] += 1
+
+    ms_dec_queued, _ = queued_time(next_decode, R, K, 20.0)
+    ms_launch = ms_dec_queued
     dec_gbps = dec_bytes_mean / (ms_launch * 1e-3) / 1e9
     # the timed region launches one kernel per step (the fused step)
     achieved = mean_step_bytes / (ms_step * 1e-3) / 1e9
@@ -350,7 +383,8 @@ def main():
                                f"contiguous cache, {R} cold replicas",
                    "B": wl.B, "S": wl.S, "H": wl.H, "G": wl.G, "d_v": wl.d_v, "d_r": wl.d_r,
                    "replicas": R, "split_tokens": split_used,
-                   "graph": use_graph, "step": "gva_decode_step (one launch)"},
+                   "timing": "K launches back to back, queued behind a spin kernel",
+                   "step": "gva_decode_step (one launch)"},
         "cache_read_GBps": round(mean_step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "step_kernel_us": round(ms_step * 1e3, 3),
         "decode_us": round(ms_launch * 1e3, 3),
@@ -358,8 +392,10 @@ def main():
         "decode_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
         "decode_event_per_call_us": round(dec_ms_mean * 1e3, 3),
         "decode_event_per_call_median_us": round(float(np.median(dec_ms)) * 1e3, 3),
+        "graph_ms_per_step": None if ms_graph is None else round(ms_graph, 6),
+        "timing_attempts": step_attempts,
         "eager_ms_per_step": round(ms_eager, 6),
-        "three_call_steps_per_s": None if ms_three is None else round(1e3 / ms_three, 2),
+        "three_call_steps_per_s": round(1e3 / ms_three, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "fused decode step",
@@ -390,7 +426,8 @@ def main():
 
 
 def measure_ceilings(read_bytes: int, replicas: int = 16):
-    """Ceilings on this GPU, graph-timed in this process (libgva_ceiling.so):
+    """Ceilings on this GPU, timed in this process (libgva_ceiling.so) as K
+    launches back to back behind a spin kernel, like the decode step:
     the per-launch floor of an empty kernel, a plain read of `read_bytes` in
     the decode's load pattern (256 workgroups, 1 KB per load instruction,
     `replicas` cold buffers), and a 2 GiB streaming read."""
@@ -417,7 +454,7 @@ def measure_ceilings(read_bytes: int, replicas: int = 16):
             "read_bytes": rb, "read_us": round(mid, 3), "read_GBps": round(rb / (mid * 1e-6) / 1e9, 1),
             "read_2GiB_us": round(big, 2), "read_2GiB_GBps": round(big_bytes / (big * 1e-6) / 1e9, 1),
             "kernel": "plain read, 1 KB per load instruction, 256 workgroups x 8 waves, "
-                      "every load of a wave requested at once; cold replicas; K launches in one graph"}
+                      "every load of a wave requested at once; cold replicas; K launches back to back behind a spin kernel"}
 
 
 def ceiling_bench(args):
@@ -628,20 +665,20 @@ def multi_compare(args):
             v, k, M = reps[i % R]
             gva.gva_decode_multi(shape, nq, q, qr, M, v, k, seq, None, wl.scale, out, ws)
 
+        host = []
         for i in range(2 * R):
+            t0 = time.perf_counter()
             call(i)
+            host.append(time.perf_counter() - t0)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(K):
-                call(i)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / K * 1e3
+        ci = [0]
+
+        def next_call():
+            call(ci[0])
+            ci[0] += 1
+
+        ms, _ = queued_time(next_call, R, K, 1e6 * float(np.median(host)))
+        us = ms * 1e3
         res[f"nq{nq}"] = {"us": round(us, 3), "cache_GBps": round(nbytes / us / 1e3, 1),
                           "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4),
                           "query_tokens_per_s": round(wl.B * nq / us * 1e6, 1)}
@@ -904,7 +941,7 @@ def measure_gva_vs_gqa(wl, K: int) -> dict:
     """gva_decode and gva_gqa_ref_decode on the same B, S, G, H and d_v = d_h:
     the GVA cache (G value rows + one positional key per token) against the
     GQA cache (G key rows + G value rows per token). Each is timed as K
-    back-to-back launches in one graph over cold replicas."""
+    back-to-back launches over cold replicas, queued behind a spin kernel."""
     import numpy as np
     import torch
 
@@ -942,20 +979,20 @@ def measure_gva_vs_gqa(wl, K: int) -> dict:
             else:
                 gva.gva_gqa_ref_decode(shape, q, b2, a, seq, None, 0.125, o, ws)
 
+        host = []
         for i in range(2 * R):
+            t0 = time.perf_counter()
             call(i)
+            host.append(time.perf_counter() - t0)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(K):
-                call(i)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / K * 1e3
+        ci = [0]
+
+        def next_call():
+            call(ci[0])
+            ci[0] += 1
+
+        ms, _ = queued_time(next_call, R, K, 1e6 * float(np.median(host)))
+        us = ms * 1e3
         out[kind] = {"us": round(us, 3), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
                      "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4), "replicas": R}
         del reps

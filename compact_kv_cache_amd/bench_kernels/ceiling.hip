@@ -27,7 +27,7 @@ constexpr int kNonTemporal = 2;
 __global__ void empty_kernel() {}
 
 // One wave that returns once `ticks` of the 100 MHz real-time counter have
-// passed: keeps the device busy while the host enqueues a timed graph.
+// passed: keeps the device busy while the host enqueues the timed launches.
 __global__ void spin_kernel(unsigned long long ticks) {
   const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
   while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) {
@@ -74,28 +74,27 @@ __global__ __launch_bounds__(512) void read_ring_kernel(const char* src, unsigne
   if (x == 0x9e3779b9u) sink[blockIdx.x] = x;
 }
 
+// K launches back to back on stream s, timed with events: the device spins
+// first while the host enqueues them (a C++ loop, a few microseconds per
+// launch), so the events bracket the device running the launches back to
+// back, as the decode step is timed. Best of three runs, after a warm-up run.
 template <typename F>
-hipError_t graph_time(hipStream_t s, int launches, F launch, double* us) {
-  hipGraph_t g = nullptr;
-  hipGraphExec_t ge = nullptr;
+hipError_t queued_time(hipStream_t s, int launches, F launch, double* us) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
-  if (e != hipSuccess) return e;
-  for (int k = 0; k < launches; ++k) launch(k);
-  e = hipStreamEndCapture(s, &g);
-  if (e == hipSuccess) e = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
-  if (e == hipSuccess) e = hipGraphLaunch(ge, s);  // warm-up replay
+  for (int k = 0; k < launches; ++k) launch(k);  // warm-up
+  hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e == hipSuccess) e = hipEventCreate(&e0);
   if (e == hipSuccess) e = hipEventCreate(&e1);
   float best = 1e30f;
   for (int rep = 0; rep < 3 && e == hipSuccess; ++rep) {
-    // the device spins for 1 ms while the host enqueues the replay, so the
-    // events bracket the launches as the device runs them back to back
-    spin_kernel<<<1, 64, 0, s>>>(100000ull);
+    spin_kernel<<<1, 64, 0, s>>>(100000ull);  // about 1 ms
     e = hipGetLastError();
     if (e == hipSuccess) e = hipEventRecord(e0, s);
-    if (e == hipSuccess) e = hipGraphLaunch(ge, s);
+    for (int k = 0; k < launches && e == hipSuccess; ++k) {
+      launch(k);
+      e = hipGetLastError();
+    }
     if (e == hipSuccess) e = hipEventRecord(e1, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     float ms = 0.f;
@@ -104,8 +103,6 @@ hipError_t graph_time(hipStream_t s, int launches, F launch, double* us) {
   }
   if (e0) (void)hipEventDestroy(e0);
   if (e1) (void)hipEventDestroy(e1);
-  if (ge) (void)hipGraphExecDestroy(ge);
-  if (g) (void)hipGraphDestroy(g);
   if (e == hipSuccess) *us = best * 1e3 / launches;
   return e;
 }
@@ -118,7 +115,7 @@ int ceiling_empty_us(int launches, double* us) {
   hipStream_t s = nullptr;
   hipError_t e = hipStreamCreate(&s);
   if (e != hipSuccess) return e;
-  e = graph_time(s, launches, [&](int) { empty_kernel<<<256, 512, 0, s>>>(); }, us);
+  e = queued_time(s, launches, [&](int) { empty_kernel<<<256, 512, 0, s>>>(); }, us);
   (void)hipStreamDestroy(s);
   return e;
 }
@@ -138,7 +135,7 @@ int ceiling_read_us(unsigned long long bytes, int replicas, int wgs, int launche
   const unsigned pw = (unsigned)per_wg;
   const bool all_at_once = per_wg <= 17 * 8 * 1024;
   if (e == hipSuccess) {
-    e = graph_time(s, launches, [&](int k) {
+    e = queued_time(s, launches, [&](int k) {
       const char* src = buf + (size_t)(k % replicas) * bytes;
       if (all_at_once)
         read_all_kernel<17><<<wgs, 512, 0, s>>>(src, pw, sink);
@@ -150,6 +147,15 @@ int ceiling_read_us(unsigned long long bytes, int replicas, int wgs, int launche
   if (sink) (void)hipFree(sink);
   if (buf) (void)hipFree(buf);
   return e;
+}
+
+// A spin of `ticks` (100 MHz) on `wgs` workgroups of one wave each, on the
+// caller's stream (a HIP stream handle; NULL is the default stream): keeps
+// every compute unit occupied while the host enqueues timed launches.
+int ceiling_spin_all(unsigned long long ticks, int wgs, void* stream) {
+  if (wgs < 1) return hipErrorInvalidValue;
+  spin_kernel<<<wgs, 64, 0, static_cast<hipStream_t>(stream)>>>(ticks);
+  return hipGetLastError();
 }
 
 }  // extern "C"
