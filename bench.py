@@ -170,7 +170,10 @@ def main():
     cache_bytes = wl.B * wl.S * bpt
     R = args.replicas or max(2, math.ceil(512e6 / cache_bytes))
     K, Wm = args.steps, args.warmup
-    total_steps = 3 * Wm + 8 * K + 8  # (queued regions may be repeated, see queued_time)
+    # every step appends a token; the queued regions may run up to three times
+    # (queued_time): 2 eager + 3 (W - 2 + K) fused + 3 K three-call + (W - 2 + K)
+    # graph + K eager steps at most
+    total_steps = 4 * Wm + 8 * K + 8
     per_rep = math.ceil(total_steps / R) + 1
     cap = wl.S + per_rep
 
