@@ -70,8 +70,11 @@ typedef enum gva_dtype {
  *                    H/G in {1, 2, 4})
  *   d_n, d_v         content-query and value widths (the kernels take 64, 64)
  *   d_r              shared positional-key width (0, 8, 16, 24 or 32)
- *   capacity         contiguous cache: token slots per sequence;
- *                    paged cache: ignored
+ *   capacity         contiguous cache: token slots per sequence (a
+ *                    multiple of 512 keeps each (sequence, group) slab on a
+ *                    64 KiB boundary; strides just past a power of two can
+ *                    cost a decode of many slabs up to a third of its time in
+ *                    memory-channel conflicts); paged cache: ignored
  *   max_seq_len      host-side upper bound of seq_lens[b] during the call
  *                    (sizes the decode grid); tokens beyond it are ignored.
  *                    Must be <= capacity (contiguous) or
