@@ -269,8 +269,9 @@ gva_status gva_prefill(const gva_shape* shape, int32_t n_q, const void* q_nope, 
  *   seq_lens int32 [B], in/out: the new token lands at seq_lens[b] and the
  *            value grows by one (clamped to the capacity as in gva_append)
  *   shape->max_seq_len must bound the lengths AFTER the append.
- *   workspace at least gva_decode_step_workspace_bytes(shape) bytes, zero
- *            before its first use, left reusable by every completed call.
+ *   workspace at least gva_decode_step_workspace_bytes(shape) bytes, 16-byte
+ *            aligned, zero before its first use, left reusable by every
+ *            completed call.
  * Other arguments as for gva_append / gva_decode.
  */
 gva_status gva_decode_step(const gva_shape* shape, const void* v_new, const void* kr_new,
