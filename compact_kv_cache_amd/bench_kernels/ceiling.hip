@@ -149,13 +149,4 @@ int ceiling_read_us(unsigned long long bytes, int replicas, int wgs, int launche
   return e;
 }
 
-// A spin of `ticks` (100 MHz) on `wgs` workgroups of one wave each, on the
-// caller's stream (a HIP stream handle; NULL is the default stream): keeps
-// every compute unit occupied while the host enqueues timed launches.
-int ceiling_spin_all(unsigned long long ticks, int wgs, void* stream) {
-  if (wgs < 1) return hipErrorInvalidValue;
-  spin_kernel<<<wgs, 64, 0, static_cast<hipStream_t>(stream)>>>(ticks);
-  return hipGetLastError();
-}
-
 }  // extern "C"
