@@ -532,6 +532,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
         }
       }
     }
+    // V^T operands of P.V, read before the scores: they depend only on the
+    // staged tile, so their LDS latency overlaps the score products and the
+    // softmax
+    Frag vts[2][4];
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vstage + tr_off[db] + (32 * pr + 16 * h) * (kD * 2)));
+          const uint2 xb = __builtin_bit_cast(uint2, x);
+          vts[pr][db].u[2 * h] = xb.x;
+          vts[pr][db].u[2 * h + 1] = xb.y;
+        }
     f32x4 s[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -588,18 +604,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
         pb.h[4 + i] = (__bf16)s[2 * pr + 1][i];
       }
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        Frag vt;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vstage + tr_off[db] + (32 * pr + 16 * h) * (kD * 2)));
-          const uint2 xb = __builtin_bit_cast(uint2, x);
-          vt.u[2 * h] = xb.x;
-          vt.u[2 * h + 1] = xb.y;
-        }
-        acc_o[db] = mma(vt, pb, acc_o[db]);
-      }
+      for (int db = 0; db < 4; ++db) acc_o[db] = mma(vts[pr][db], pb, acc_o[db]);
     }
   };
 
