@@ -119,7 +119,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="mid_bf16")
     p.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = enough for 512 MB)")
-    p.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the graph-replay figure, the GQA comparison and the ceilings")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--split", type=int, default=-1,
