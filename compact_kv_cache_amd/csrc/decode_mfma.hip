@@ -749,6 +749,31 @@ __global__ __launch_bounds__(64 * kWaves, 2) void decode_mfma_kernel(const void*
       if ((tid >> 6) + u * kWaves < NCOL) out[orow[u] * kD + d] = (__bf16)(l[u] > 0.f ? o[u] / l[u] : 0.f);
     return;
   }
+  if constexpr (!PP2 && !STEP) {
+    // Decode: each wave that owns output rows (rows w + 8u) hands off on its
+    // own, with no workgroup barrier: it waits for its own partial stores'
+    // acknowledgement and arrives on its own counter (slot 4w of the group's
+    // counter line, which stays zero between calls); the last arrival merges
+    // those rows. (The fused step keeps the workgroup-wide arrival below:
+    // there this form measured about 0.1 us slower at the mid shape, against
+    // 0.1-0.2 us faster for the decode.)
+    constexpr int kOwn = NCOL < kWaves ? NCOL : kWaves;
+    static_assert(4 * kWaves <= kCounterStride, "one counter slot per wave on the group's line");
+    if (w >= kOwn) return;
+    store_partial(split);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
+    int32_t* wcounter = a.counters + ((int64_t)b * G + g) * kCounterStride + 4 * w;
+    int ticket = 0;
+    if (lane == 0) ticket = __hip_atomic_fetch_add(wcounter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ticket = __builtin_amdgcn_readfirstlane(ticket);
+    if (ticket != n_parts - 1) return;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (w + u * kWaves < NCOL)
+        out[orow[u] * kD + d] = (__bf16)merge_partials(a.ws_o, a.ws_ml, orow[u] * a.n_split, n_parts, d);
+    if (lane == 0) reset_counter(wcounter);
+    return;
+  }
   store_partial(split);
   // partitions of the range that hold tokens (uniform)
   const int arrivals = min(split + n_own, n_parts) - split;
